@@ -1,0 +1,238 @@
+"""Workload recipes and the seeded generator.
+
+Shapes follow DeepSeek-V3/R1 as the pages give them: n_h = 128 heads, a
+576-element cache row (d_c = 512 latent + d_R = 64 RoPE, "DeepSeek R1
+Architecture & Deployment Guide" section 1.1), page blocks of 64 tokens
+("DeepSeek-R1" record, engine kernel constraint (1)) and the FP8 row of
+constraint (2).  The five named workloads are the ones the decode is measured
+and parity-checked on; the ``*_small`` variants keep each recipe but shrink
+batch and lengths so the float64 oracle finishes in seconds.
+
+Draw order (torch CPU generator, seeded per workload):
+  1. seq_lens
+  2. physical page permutation (unless the table is the identity)
+  3. cache source values: float32 N(0,1), drawn in chunks of 256 pages
+     (for FP8 first an outlier mask per chunk, then the values), then
+     rounded to bf16 (round-to-nearest-even) or quantised to FP8
+  4. queries: float32 N(0,1) times the workload's q scale, rounded to bf16
+
+Poisoning (never read by a correct decode): tail slots after the last token
+of each sequence, every spare page, and FP8 row padding.  bf16 poison is the
+NaN pattern 0x7FC0; FP8 poison is code 0x7F (NaN) and scale 0xFF (NaN).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+import torch
+
+BF16_NAN = 0x7FC0
+FP8_CODE_NAN = 0x7F
+E8M0_NAN = 0xFF
+GEN_CHUNK_PAGES = 256
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadSpec:
+    name: str
+    batch: int
+    seq_lens: Union[Tuple[str, int, int], Tuple[str, Tuple[int, ...]]]
+    kv_dtype: str = "bf16"          # "bf16" | "fp8"
+    s_q: int = 1
+    n_h: int = 128
+    d_c: int = 512
+    d_r: int = 64
+    page: int = 64
+    table: str = "perm"             # "perm" | "identity"
+    q_scale: float = 1.0
+    outlier_p: float = 0.0
+    outlier_mult: float = 1.0
+    spare_pages: int = 64
+    seed: int = 0
+    softmax_scale: float = 1.0 / math.sqrt(192.0)
+
+    @property
+    def d(self) -> int:
+        return self.d_c + self.d_r
+
+
+@dataclasses.dataclass
+class Workload:
+    spec: WorkloadSpec
+    q_bits: np.ndarray          # uint16 [B, s_q, n_h, D]
+    pool: np.ndarray            # bf16: uint16 [P, page, D]; fp8: uint8 [P, page, stride]
+    block_table: np.ndarray     # int32 [B, max_blocks]
+    seq_lens: np.ndarray        # int32 [B]
+    row_stride: int             # bytes per cached row
+
+    @property
+    def kv_bytes_algorithmic(self) -> int:
+        """Bytes of cache payload the decode must read: sum_b L_b x row payload."""
+        per_row = 2 * self.spec.d if self.spec.kv_dtype == "bf16" else self.spec.d + self.spec.d // 32
+        return int(self.seq_lens.astype(np.int64).sum()) * per_row
+
+
+def fp8_row_stride(d: int) -> int:
+    """FP8 row stride: payload (d codes + d/32 scales) rounded up to 16 bytes."""
+    payload = d + d // 32
+    return (payload + 15) // 16 * 16
+
+
+SPECS = {
+    # batch 1, 1024 tokens, contiguous cache (identity block table)
+    "single_1k": WorkloadSpec("single_1k", 1, ("fixed", (1024,)), table="identity",
+                              spare_pages=0, seed=1),
+    # paged bf16, batch 32, lengths uniform in [1024, 8192]
+    "paged_b32": WorkloadSpec("paged_b32", 32, ("uniform", 1024, 8192), seed=2),
+    # long context bf16, batch 4, q scaled by 0.5
+    "long_ctx_b4": WorkloadSpec("long_ctx_b4", 4, ("fixed", (32768, 65536, 131072, 131072)),
+                                q_scale=0.5, seed=3),
+    # FP8 latent cache, batch 64, lengths uniform in [2048, 16384], 1% outliers x20
+    "fp8_b64": WorkloadSpec("fp8_b64", 64, ("uniform", 2048, 16384), kv_dtype="fp8",
+                            outlier_p=0.01, outlier_mult=20.0, seed=4),
+    # two queries per sequence (MTP-style), causal over the last two positions
+    "mtp2_b128": WorkloadSpec("mtp2_b128", 128, ("loguniform", 512, 32768), s_q=2, seed=5),
+}
+
+# reduced-size variants of the same recipes for element-by-element parity
+SPECS.update({
+    "single_1k_small": dataclasses.replace(SPECS["single_1k"], name="single_1k_small"),
+    "paged_b32_small": dataclasses.replace(SPECS["paged_b32"], name="paged_b32_small", batch=5,
+                                           seq_lens=("uniform", 65, 1500), spare_pages=8),
+    "long_ctx_b4_small": dataclasses.replace(SPECS["long_ctx_b4"], name="long_ctx_b4_small",
+                                             batch=3, seq_lens=("fixed", (2048, 4096, 7001)),
+                                             spare_pages=8),
+    "fp8_b64_small": dataclasses.replace(SPECS["fp8_b64"], name="fp8_b64_small", batch=5,
+                                         seq_lens=("uniform", 100, 2100), spare_pages=8),
+    "mtp2_b128_small": dataclasses.replace(SPECS["mtp2_b128"], name="mtp2_b128_small", batch=6,
+                                           seq_lens=("loguniform", 40, 1500), spare_pages=8),
+})
+
+# the long-context workload is the one the bandwidth target is stated on
+BENCH_SPEC = "long_ctx_b4"
+
+
+def _draw_seq_lens(spec: WorkloadSpec, gen: torch.Generator) -> np.ndarray:
+    kind = spec.seq_lens[0]
+    if kind == "fixed":
+        vals = np.asarray(spec.seq_lens[1], dtype=np.int64)
+        if vals.size != spec.batch:
+            raise ValueError("fixed seq_lens must list one length per sequence")
+        return vals.astype(np.int32)
+    lo, hi = int(spec.seq_lens[1]), int(spec.seq_lens[2])
+    if kind == "uniform":
+        return torch.randint(lo, hi + 1, (spec.batch,), generator=gen).numpy().astype(np.int32)
+    if kind == "loguniform":
+        u = torch.rand(spec.batch, generator=gen, dtype=torch.float64).numpy()
+        vals = np.rint(np.exp(math.log(lo) + u * (math.log(hi) - math.log(lo))))
+        return np.clip(vals, lo, hi).astype(np.int32)
+    raise ValueError(f"unknown seq_lens kind {kind!r}")
+
+
+def quantize_fp8_rows(x: torch.Tensor, d: int, stride: int) -> np.ndarray:
+    """Encode float32 rows [N, d] into FP8 cache rows [N, stride] (uint8).
+
+    Per row and per group of 32 consecutive values: e = ceil(log2(amax/448))
+    + 127 clamped to [0, 254] (127 when the group is all zero); codes are the
+    values divided by 2^(e-127), clamped to +-448 and rounded to e4m3fn by
+    torch's cast.  Padding bytes are set to 0xFF.
+    """
+    n = x.shape[0]
+    g = x.reshape(n, d // 32, 32).to(torch.float64)
+    amax = g.abs().amax(dim=-1)
+    mant, ex = torch.frexp(amax / 448.0)
+    ceil_log2 = torch.where(mant == 0.5, ex - 1, ex).to(torch.int64)
+    e = torch.clamp(ceil_log2 + 127, 0, 254)
+    e = torch.where(amax == 0, torch.full_like(e, 127), e)
+    scale = torch.ldexp(torch.ones_like(amax), e - 127)
+    codes = torch.clamp(g / scale[..., None], -448.0, 448.0).to(torch.float32)
+    codes = codes.to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, d)
+    out = np.full((n, stride), E8M0_NAN, dtype=np.uint8)
+    out[:, :d] = codes.numpy()
+    out[:, d:d + d // 32] = e.to(torch.uint8).numpy()
+    return out
+
+
+def make_workload(spec: Union[str, WorkloadSpec], seed: Optional[int] = None) -> Workload:
+    if isinstance(spec, str):
+        spec = SPECS[spec]
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(spec.seed if seed is None else seed)
+    page, d = spec.page, spec.d
+
+    # 1. sequence lengths
+    seq_lens = _draw_seq_lens(spec, gen)
+    pages_per_seq = (seq_lens.astype(np.int64) + page - 1) // page
+    n_used = int(pages_per_seq.sum())
+    pool_pages = n_used + spec.spare_pages
+
+    # 2. physical placement of logical pages
+    if spec.table == "identity":
+        phys = np.arange(n_used, dtype=np.int64)
+    else:
+        phys = torch.randperm(pool_pages, generator=gen)[:n_used].numpy().astype(np.int64)
+    max_blocks = int(pages_per_seq.max()) if spec.batch else 1
+    block_table = np.full((spec.batch, max(max_blocks, 1)), -1, dtype=np.int32)
+    starts = np.concatenate([[0], np.cumsum(pages_per_seq)])
+    for b in range(spec.batch):
+        block_table[b, :pages_per_seq[b]] = phys[starts[b]:starts[b + 1]]
+
+    # 3. cache values, in logical page order
+    if spec.kv_dtype == "bf16":
+        row_stride = 2 * d
+        pool = np.full((pool_pages, page, d), BF16_NAN, dtype=np.uint16)
+    elif spec.kv_dtype == "fp8":
+        row_stride = fp8_row_stride(d)
+        pool = np.full((pool_pages, page, row_stride), E8M0_NAN, dtype=np.uint8)
+        pool[:, :, :d] = FP8_CODE_NAN
+    else:
+        raise ValueError(spec.kv_dtype)
+    for c0 in range(0, n_used, GEN_CHUNK_PAGES):
+        c1 = min(c0 + GEN_CHUNK_PAGES, n_used)
+        rows = (c1 - c0) * page
+        if spec.kv_dtype == "fp8" and spec.outlier_p > 0:
+            mask = torch.rand((rows, d), generator=gen) < spec.outlier_p
+            vals = torch.randn((rows, d), generator=gen)
+            vals = torch.where(mask, vals * spec.outlier_mult, vals)
+        else:
+            vals = torch.randn((rows, d), generator=gen)
+        if spec.kv_dtype == "bf16":
+            enc = vals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            pool[phys[c0:c1]] = enc.reshape(c1 - c0, page, d)
+        else:
+            enc = quantize_fp8_rows(vals, d, row_stride)
+            pool[phys[c0:c1]] = enc.reshape(c1 - c0, page, row_stride)
+
+    # poison tail slots after each sequence's last token
+    for b in range(spec.batch):
+        L = int(seq_lens[b])
+        if L % page and pages_per_seq[b]:
+            last = phys[starts[b] + pages_per_seq[b] - 1]
+            if spec.kv_dtype == "bf16":
+                pool[last, L % page:, :] = BF16_NAN
+            else:
+                pool[last, L % page:, :d] = FP8_CODE_NAN
+                pool[last, L % page:, d:] = E8M0_NAN
+
+    # 4. queries
+    qf = torch.randn((spec.batch, spec.s_q, spec.n_h, d), generator=gen) * spec.q_scale
+    q_bits = qf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+    return Workload(spec=spec, q_bits=q_bits, pool=pool, block_table=block_table,
+                    seq_lens=seq_lens, row_stride=row_stride)
+
+
+def to_torch(w: Workload, device) -> dict:
+    """Device tensors for the decode call (plain copies of the same bytes)."""
+    q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(device)
+    pool_bytes = torch.from_numpy(np.ascontiguousarray(w.pool).view(np.uint8)).to(device)
+    return {
+        "q": q.contiguous(),
+        "kv": pool_bytes.contiguous(),
+        "block_table": torch.from_numpy(w.block_table).to(device).contiguous(),
+        "seq_lens": torch.from_numpy(w.seq_lens).to(device).contiguous(),
+    }

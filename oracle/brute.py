@@ -1,0 +1,75 @@
+"""Pure-Python brute force for tiny inputs.
+
+Test infrastructure only (see ``oracle/__init__``).
+
+It walks the same definition as ``oracle.mla`` (guide section 1.1: score =
+scale * (q_abs . c + q_R . k_R), softmax over visible tokens, output the
+softmax-weighted latents) one scalar at a time, with ``math.exp`` and plain
+loops, and reads the cache through its own decoding path: bf16 through
+``struct`` and FP8 through torch's float8_e4m3fn / float8_e8m0fnu dtypes, not
+through the oracle's lookup tables.  It therefore checks the vectorised
+oracle's gathering, slicing, masking and reductions independently.
+"""
+
+from __future__ import annotations
+
+import math
+import struct
+
+import numpy as np
+
+
+def _bf16(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def _fp8_row_values(row_bytes, d: int):
+    import torch  # library routine for the byte formats
+    raw = torch.tensor(list(int(x) for x in row_bytes[:d + d // 32]), dtype=torch.uint8)
+    codes = raw[:d].view(torch.float8_e4m3fn).to(torch.float64).tolist()
+    scales = raw[d:].view(torch.float8_e8m0fnu).to(torch.float64).tolist()
+    return [codes[i] * scales[i // 32] for i in range(d)]
+
+
+def _row_values(pool, page_id: int, slot: int, kv_dtype: str, d: int):
+    row = pool[page_id][slot]
+    if kv_dtype == "bf16":
+        return [_bf16(row[i]) for i in range(d)]
+    return _fp8_row_values(row, d)
+
+
+def mla_decode_brute(q_bits, pool, block_table, seq_lens, *, kv_dtype: str, d_c: int,
+                     d_r: int, page: int, softmax_scale: float):
+    B, s_q, n_h, d = np.asarray(q_bits).shape
+    out = [[[[0.0] * d_c for _ in range(n_h)] for _ in range(s_q)] for _ in range(B)]
+    lse = [[[0.0] * n_h for _ in range(s_q)] for _ in range(B)]
+    for b in range(B):
+        L = int(seq_lens[b])
+        rows = []
+        for t in range(L):
+            rows.append(_row_values(pool, int(block_table[b][t // page]), t % page, kv_dtype, d))
+        for j in range(s_q):
+            n_vis = max(L - s_q + 1 + j, 0)
+            for h in range(n_h):
+                q = [_bf16(x) for x in q_bits[b][j][h]]
+                if n_vis == 0:
+                    lse[b][j][h] = -math.inf
+                    continue
+                scores = []
+                for t in range(n_vis):
+                    acc = 0.0
+                    for i in range(d_c):
+                        acc += q[i] * rows[t][i]
+                    for i in range(d_c, d_c + d_r):
+                        acc += q[i] * rows[t][i]
+                    scores.append(softmax_scale * acc)
+                m = max(scores)
+                w = [math.exp(s - m) for s in scores]
+                z = sum(w)
+                for i in range(d_c):
+                    acc = 0.0
+                    for t in range(n_vis):
+                        acc += w[t] * rows[t][i]
+                    out[b][j][h][i] = acc / z
+                lse[b][j][h] = m + math.log(z)
+    return np.array(out, dtype=np.float64), np.array(lse, dtype=np.float64)
