@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""MLA latent-cache decode throughput on one MI355X.
+
+One step = one call of the whole hot path (work planner, split-KV decode,
+LSE combine) over one batch of the long-context workload: batch 4, seq_lens
+{32768, 65536, 131072, 131072}, n_h 128, d_c 512, d_R 64, bf16 paged cache
+(block 64, permuted pages).  Inputs are seeded synthetic data already
+resident in HBM before the timed region.
+
+Prints one JSON line: KV-read GB/s (whole job), TFLOP/s, the dominant
+kernel's roofline (decode kernel: algorithmic KV bytes per launch over its
+average event-timed duration) and the float64 CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+FLOP_PER_ROW_TOKEN = 2 * 576 + 2 * 512   # Q.K^T over the 576-wide row + P.V over 512
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the long-context one)")
+    ap.add_argument("--num-workers", type=int, default=0)
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="oracle sample budget (seconds)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def flops_per_step(w) -> int:
+    s = w.spec
+    tot = 0
+    for L in w.seq_lens.tolist():
+        for j in range(s.s_q):
+            tot += max(L - s.s_q + 1 + j, 0)
+    return tot * s.n_h * FLOP_PER_ROW_TOKEN
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The float64 oracle as it stands, on whole sequences of the same workload
+    until the time budget is used (always at least one sequence)."""
+    import numpy as np
+    from oracle import mla_decode_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    s = w.spec
+    row_bytes = 2 * s.d if s.kv_dtype == "bf16" else s.d + s.d // 32
+    done, nbytes = [], 0
+    t0 = time.perf_counter()
+    for b in range(s.batch):
+        mla_decode_ref(w.q_bits, w.pool, w.block_table, w.seq_lens, kv_dtype=s.kv_dtype, d_c=s.d_c,
+                       d_r=s.d_r, page=s.page, softmax_scale=s.softmax_scale, batches=[b])
+        done.append(b)
+        nbytes += int(w.seq_lens[b]) * row_bytes
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"sequences {done} of {s.name} (all {s.n_h} heads, {sum(int(w.seq_lens[b]) for b in done)} "
+                      f"tokens), float64 numpy oracle, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this decode runs on one GPU; multi-GPU runs are not part of this build "
+              "(the batch would shard by sequence with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mla_inputs import SPECS, BENCH_SPEC, make_workload, to_torch
+    import mla_latent_cache_decode_amd as mla
+
+    name = args.workload or BENCH_SPEC
+    print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+    w = make_workload(name)
+    s = w.spec
+    dev = torch.device("cuda:0")
+    t = to_torch(w, dev)
+    dec = mla.MlaDecode(max_batch=s.batch, s_q=s.s_q, n_h=s.n_h, d_c=s.d_c, d_r=s.d_r, block_size=s.page,
+                        max_blocks_per_seq=w.block_table.shape[1], kv_dtype=s.kv_dtype,
+                        softmax_scale=s.softmax_scale, num_workers=args.num_workers)
+    ws = dec.alloc_workspace(s.batch, device=dev)
+    out = torch.empty((s.batch, s.s_q, s.n_h, s.d_c), dtype=torch.float32, device=dev)
+    lse = torch.empty((s.batch, s.s_q, s.n_h), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    lib = mla.load_library()
+    call = (dec._h, t["q"].data_ptr(), t["kv"].data_ptr(), t["block_table"].data_ptr(),
+            t["seq_lens"].data_ptr(), s.batch, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(),
+            stream.cuda_stream)
+
+    def step():
+        st = lib.mla_decode_run(*call)
+        if st != 0:
+            raise mla.MlaError(st, "mla_decode_run")
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-step events around the decode kernel (recorded by the library on this stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        b.record(stream)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t_start.record(stream)
+    for k in range(args.steps):
+        lib.mla_decode_set_profile_events(dec._h, ev[k][0].cuda_event, ev[k][1].cuda_event)
+        step()
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    lib.mla_decode_set_profile_events(dec._h, None, None)
+    ms_total = t_start.elapsed_time(t_stop)
+    ms_step = ms_total / args.steps
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    kms = float(np.mean(kernel_ms))
+
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    kv_bytes = w.kv_bytes_algorithmic
+    gbs = kv_bytes / (ms_step * 1e-3) / 1e9
+    fl = flops_per_step(w)
+    tflops = fl / (ms_step * 1e-3) / 1e12
+    k_gbs = kv_bytes / (kms * 1e-3) / 1e9
+    info = dec.info()
+    res = {
+        "metric": "MLA decode KV-read GB/s (% of HBM peak) + TFLOP/s, n_h=128, 1 GPU",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.kv_dtype == "bf16" else "fp8-e4m3/e8m0 cache, bf16 mfma",
+        "data": "synthetic (seeded N(0,1) cache and queries, DeepSeek-V3/R1 shapes)",
+        "config": {"workload": s.name, "batch": s.batch, "s_q": s.s_q, "n_h": s.n_h, "d_c": s.d_c,
+                   "d_r": s.d_r, "page": s.page, "kv_dtype": s.kv_dtype,
+                   "seq_lens": w.seq_lens.tolist() if s.batch <= 8 else f"{s.seq_lens}",
+                   "total_tokens": int(w.seq_lens.sum()), "kv_bytes": kv_bytes,
+                   "workers": info["num_workers"], "row_groups": info["row_groups"],
+                   "compute_units": info["compute_units"]},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tflop_s": round(tflops, 2),
+        "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mla_decode_kernel", "kernel_ms": round(kms, 5),
+                     "bytes_per_launch": kv_bytes},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

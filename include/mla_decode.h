@@ -1,0 +1,175 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) MLA latent-cache decode library.
+ *
+ * Operation ("DeepSeek R1 Architecture & Deployment Guide", section 1.1):
+ * every cached token holds ONE row shared by all attention heads, the
+ * concatenation of the compressed latent c (d_c values) and the decoupled,
+ * already-rotated RoPE key k_R (d_r values).  With the key up-projection
+ * absorbed into the query and the value up-projection absorbed into the
+ * output projection (applied by the caller afterwards), head h of query j of
+ * sequence b computes
+ *
+ *     s_t  = softmax_scale * ( q_abs . c_t + q_R . k_R_t )      for visible t
+ *     out  = sum_t softmax(s)_t * c_t                            (d_c floats)
+ *     lse  = ln sum_t exp(s_t)
+ *
+ * The cache is paged: the "DeepSeek-R1" record, engine kernel constraint (1),
+ * instantiates MLA decode per page-block size and names 64; constraint (2)
+ * gives the FP8 row (e4m3 codes over every dimension, RoPE included, plus one
+ * e8m0 scale per 32 codes).
+ *
+ * Conventions shared by every entry point:
+ *   - All device pointers are plain device addresses owned by the caller
+ *     (this library allocates no device memory).  Host pointers are marked.
+ *   - No entry point aborts, prints or throws; every failure is a status.
+ *   - Entry points that launch work are asynchronous on the caller's HIP
+ *     stream (passed as void*, NULL = the default stream) and never
+ *     synchronise; a device fault surfaces at the caller's next sync.
+ *   - The library is silent; MLA_DECODE_LOG=1 in the environment makes
+ *     mla_decode_init print the chosen plan to stderr.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_DECODE_ABI_VERSION 1
+
+typedef enum mla_status {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARGUMENT = 1,    /* null/misaligned pointer, bad size or field */
+    MLA_ERR_UNSUPPORTED = 2,         /* valid request this build does not implement */
+    MLA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < mla_decode_workspace_size */
+    MLA_ERR_HIP = 4,                 /* a HIP runtime call failed (incl. no device) */
+    MLA_ERR_OUT_OF_MEMORY = 5        /* host allocation of the handle failed */
+} mla_status_t;
+
+/* Cache row formats.
+ * MLA_KV_BF16: a row is d_c + d_r bf16 values, c first then k_R
+ *   (guide section 1.1 concat order); row stride 2*(d_c+d_r) bytes.
+ * MLA_KV_FP8_E4M3_E8M0: a row is D = d_c + d_r e4m3fn codes (c then k_R),
+ *   then D/32 e8m0 scale bytes, scale g multiplying codes 32g..32g+31
+ *   ("DeepSeek-R1" record, constraint (2)); value = e4m3(code) * 2^(e-127);
+ *   the row is padded to a 16-byte stride (608 bytes at D = 576; 528 bytes,
+ *   no padding, at D = 512).  Padding bytes are never read. */
+typedef enum mla_kv_dtype {
+    MLA_KV_BF16 = 0,
+    MLA_KV_FP8_E4M3_E8M0 = 1
+} mla_kv_dtype_t;
+
+/* Flags for mla_decode_params_t.flags */
+#define MLA_FLAG_NONE 0
+
+typedef struct mla_decode_params {
+    int32_t struct_size;        /* = sizeof(mla_decode_params_t); guards ABI evolution     */
+    int32_t max_batch;          /* upper bound on the run-time batch, >= 1                  */
+    int32_t s_q;                /* queries per sequence (1 = plain decode, 2 = MTP), 1..8   */
+    int32_t n_h;                /* heads, a multiple of 32, <= 1024                         */
+    int32_t d_c;                /* latent width; this build: 512                            */
+    int32_t d_r;                /* RoPE key width; this build: 64                           */
+    int32_t block_size;         /* tokens per page; this build: 64                          */
+    int32_t max_blocks_per_seq; /* row stride (in entries) of block_table, >= 1             */
+    int32_t kv_dtype;           /* an mla_kv_dtype_t                                        */
+    float   softmax_scale;      /* multiplies q.row; finite and > 0 (e.g. 1/sqrt(192))      */
+    int32_t num_workers;        /* 0 = one worker per compute unit (chosen at init);
+                                   > 0 forces that many context-split workers (tests,
+                                   sweeps); at most 65536                                   */
+    int32_t flags;              /* MLA_FLAG_*                                               */
+} mla_decode_params_t;
+
+typedef struct mla_decode_handle* mla_decode_handle_t;
+
+/* mla_decode_init -- validate params, query the current HIP device, choose the
+ * kernel instance and the split plan bounds.
+ *   params : host pointer, read only during the call.
+ *   out    : host pointer; receives a host-only handle (immutable except
+ *            through mla_decode_set_profile_events) on MLA_OK, NULL otherwise.
+ * Every field is validated on the host BEFORE any HIP call
+ * (MLA_ERR_INVALID_ARGUMENT / MLA_ERR_UNSUPPORTED).  Then the current device
+ * must be a gfx950; otherwise MLA_ERR_UNSUPPORTED, and MLA_ERR_HIP if no
+ * device can be queried.  The handle is bound to the device current at init. */
+mla_status_t mla_decode_init(const mla_decode_params_t* params, mla_decode_handle_t* out);
+
+/* mla_decode_workspace_size -- device workspace bytes that mla_decode_run needs
+ * for `batch` sequences (0 <= batch <= max_batch).  `bytes` is a host pointer.
+ * The workspace holds the per-call work plan and the split-KV partial results
+ * (fp32 outputs and LSEs of every context split). */
+mla_status_t mla_decode_workspace_size(mla_decode_handle_t h, int32_t batch, size_t* bytes);
+
+/* mla_decode_run -- one decode step for `batch` sequences, all heads, all queries.
+ *   q           : device, bf16 [batch][s_q][n_h][d_c + d_r], each row q_abs then q_R
+ *                 (scale not applied), 16-byte aligned.
+ *   kv_pages    : device, [num_pages][block_size][row_stride] in kv_dtype's row
+ *                 format (see mla_kv_row_stride), 16-byte aligned.
+ *   block_table : device, int32 [batch][max_blocks_per_seq]; entry [b][p] is the
+ *                 physical page of logical page p of sequence b.  Only entries
+ *                 p < ceil(seq_lens[b] / block_size) are read; they must be valid
+ *                 page indices (precondition, not checked on the device).
+ *   seq_lens    : device, int32 [batch]; L_b counts every cached token including
+ *                 the s_q new ones.  Query j of sequence b sees tokens
+ *                 0 .. L_b - s_q + j (causal over the last s_q positions).
+ *                 Precondition 0 <= L_b <= block_size * max_blocks_per_seq; a
+ *                 query that sees no token gets out = 0 and lse = -inf.
+ *   batch       : 0 <= batch <= max_batch; 0 is a no-op.
+ *   out         : device, fp32 [batch][s_q][n_h][d_c], 16-byte aligned.
+ *   lse         : device, fp32 [batch][s_q][n_h] natural-log LSE, or NULL.
+ *   workspace   : device, >= mla_decode_workspace_size(batch) bytes, 256-byte
+ *                 aligned; contents need not be initialised and are scratch
+ *                 after the call.  Concurrent runs need distinct workspaces.
+ *   hip_stream  : hipStream_t as void*, NULL = default stream.
+ * Tail slots after a sequence's last token, unused pages and row padding are
+ * never read, whatever they hold.  Results do not depend on how the context
+ * is split across workers beyond fp32 rounding, and repeated calls with the
+ * same inputs and handle are bitwise identical. */
+mla_status_t mla_decode_run(mla_decode_handle_t h,
+                            const void* q,
+                            const void* kv_pages,
+                            const int32_t* block_table,
+                            const int32_t* seq_lens,
+                            int32_t batch,
+                            float* out,
+                            float* lse,
+                            void* workspace,
+                            size_t workspace_bytes,
+                            void* hip_stream);
+
+/* mla_decode_set_profile_events -- measurement hook.  When both are non-NULL,
+ * later runs record ev_start immediately before and ev_stop immediately after
+ * the split-KV decode kernel (not the planner or combine) on the run's stream.
+ * Both are hipEvent_t passed as void*, owned by the caller.  NULL, NULL turns
+ * the hook off.  Not thread-safe with concurrent runs on the same handle. */
+mla_status_t mla_decode_set_profile_events(mla_decode_handle_t h, void* ev_start, void* ev_stop);
+
+/* mla_decode_get_info -- host copies of the plan bounds chosen at init.
+ * Any output pointer may be NULL. */
+mla_status_t mla_decode_get_info(mla_decode_handle_t h, int32_t* num_workers,
+                                 int32_t* row_groups, int32_t* compute_units);
+
+/* mla_decode_free -- release the host handle (no device memory is held).
+ * NULL is accepted. */
+mla_status_t mla_decode_free(mla_decode_handle_t h);
+
+/* mla_kv_row_bytes -- payload bytes of one cached row: 2*(d_c+d_r) for bf16,
+ * (d_c+d_r) + (d_c+d_r)/32 for FP8 (594 at 576 dims, 528 at 512 dims).
+ * Returns 0 for an invalid combination. */
+size_t mla_kv_row_bytes(int32_t kv_dtype, int32_t d_c, int32_t d_r);
+
+/* mla_kv_row_stride -- row stride in a page: the payload rounded up to 16 bytes
+ * (1152 bf16, 608 FP8 at 576 dims).  Returns 0 for an invalid combination. */
+size_t mla_kv_row_stride(int32_t kv_dtype, int32_t d_c, int32_t d_r);
+
+/* mla_status_string -- static, never NULL. */
+const char* mla_status_string(mla_status_t s);
+
+/* mla_decode_abi_version -- MLA_DECODE_ABI_VERSION of the built library. */
+int32_t mla_decode_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_DECODE_H */

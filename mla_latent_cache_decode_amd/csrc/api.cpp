@@ -1,0 +1,248 @@
+// C ABI of the MLA decode library (declared in include/mla_decode.h).
+//
+// Host responsibilities: validate every argument before touching HIP, query
+// the device once at init, size the workspace, and enqueue planner -> decode
+// -> combine on the caller's stream without synchronising.  All device
+// memory is the caller's.
+#include "mla_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "mla_internal.h"
+
+struct mla_decode_handle {
+    mla_decode_params_t p;
+    int device;
+    int compute_units;
+    int num_workers;
+    int row_groups;
+    int rows;                  // M = s_q * n_h
+    int partial_slots;         // upper bound on partial results
+    hipEvent_t ev_start;
+    hipEvent_t ev_stop;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kOverheadUnits = 2;    // per-segment cost of query load + epilogue, in pages
+constexpr int kMinQuota = 1;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+    size_t header, segs, seg_worker, worker_start, seq_nsplit, seq_slot, part_lse, part_o, total;
+};
+
+WsLayout layout(const mla_decode_handle* h, int32_t batch) {
+    WsLayout l{};
+    const size_t nseg = (size_t)h->num_workers + (size_t)batch;
+    size_t off = 0;
+    l.header = off;        off += align_up(16 * sizeof(int32_t));
+    l.segs = off;          off += align_up(nseg * sizeof(int4));
+    l.seg_worker = off;    off += align_up(nseg * sizeof(int32_t));
+    l.worker_start = off;  off += align_up(((size_t)h->num_workers + 1) * sizeof(int32_t));
+    l.seq_nsplit = off;    off += align_up((size_t)(batch > 0 ? batch : 1) * sizeof(int32_t));
+    l.seq_slot = off;      off += align_up((size_t)(batch > 0 ? batch : 1) * sizeof(int32_t));
+    l.part_lse = off;      off += align_up((size_t)h->partial_slots * h->rows * sizeof(float));
+    l.part_o = off;        off += align_up((size_t)h->partial_slots * h->rows * mla::kDc * sizeof(float));
+    l.total = off;
+    return l;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+mla_status_t validate_params(const mla_decode_params_t* p) {
+    if (p->struct_size != (int32_t)sizeof(mla_decode_params_t)) return MLA_ERR_INVALID_ARGUMENT;
+    if (p->max_batch < 1 || p->max_batch > (1 << 20)) return MLA_ERR_INVALID_ARGUMENT;
+    if (p->s_q < 1 || p->s_q > 8) return MLA_ERR_INVALID_ARGUMENT;
+    if (p->n_h < 32 || p->n_h > 1024 || p->n_h % 32 != 0) return MLA_ERR_INVALID_ARGUMENT;
+    if (p->d_c <= 0 || p->d_r < 0 || p->block_size <= 0) return MLA_ERR_INVALID_ARGUMENT;
+    if (p->max_blocks_per_seq < 1) return MLA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)p->max_blocks_per_seq * p->block_size > (int64_t)1 << 30) return MLA_ERR_INVALID_ARGUMENT;
+    if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3_E8M0) return MLA_ERR_INVALID_ARGUMENT;
+    if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
+    if (p->num_workers < 0 || p->num_workers > 65536) return MLA_ERR_INVALID_ARGUMENT;
+    if (p->flags != MLA_FLAG_NONE) return MLA_ERR_INVALID_ARGUMENT;
+    if ((p->d_c + p->d_r) % 32 != 0 && p->kv_dtype == MLA_KV_FP8_E4M3_E8M0) return MLA_ERR_INVALID_ARGUMENT;
+    // valid requests outside what this build instantiates
+    if (p->d_c != mla::kDc || p->d_r != mla::kDr) return MLA_ERR_UNSUPPORTED;
+    if (p->block_size != mla::kPage) return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_decode_abi_version(void) { return MLA_DECODE_ABI_VERSION; }
+
+const char* mla_status_string(mla_status_t s) {
+    switch (s) {
+        case MLA_OK: return "MLA_OK";
+        case MLA_ERR_INVALID_ARGUMENT: return "MLA_ERR_INVALID_ARGUMENT";
+        case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+        case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+        case MLA_ERR_HIP: return "MLA_ERR_HIP";
+        case MLA_ERR_OUT_OF_MEMORY: return "MLA_ERR_OUT_OF_MEMORY";
+    }
+    return "MLA_ERR_UNKNOWN";
+}
+
+size_t mla_kv_row_bytes(int32_t kv_dtype, int32_t d_c, int32_t d_r) {
+    if (d_c <= 0 || d_r < 0) return 0;
+    const size_t d = (size_t)d_c + (size_t)d_r;
+    if (kv_dtype == MLA_KV_BF16) return 2 * d;
+    if (kv_dtype == MLA_KV_FP8_E4M3_E8M0) return d % 32 ? 0 : d + d / 32;
+    return 0;
+}
+
+size_t mla_kv_row_stride(int32_t kv_dtype, int32_t d_c, int32_t d_r) {
+    const size_t b = mla_kv_row_bytes(kv_dtype, d_c, d_r);
+    return (b + 15) / 16 * 16;
+}
+
+mla_status_t mla_decode_init(const mla_decode_params_t* params, mla_decode_handle_t* out) {
+    if (out) *out = nullptr;
+    if (!params || !out) return MLA_ERR_INVALID_ARGUMENT;
+    const mla_status_t v = validate_params(params);
+    if (v != MLA_OK) return v;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MLA_ERR_UNSUPPORTED;
+
+    mla_decode_handle* h = new (std::nothrow) mla_decode_handle;
+    if (!h) return MLA_ERR_OUT_OF_MEMORY;
+    std::memset(h, 0, sizeof(*h));
+    h->p = *params;
+    h->device = dev;
+    h->compute_units = prop.multiProcessorCount;
+    h->rows = params->s_q * params->n_h;
+    h->row_groups = (h->rows + mla::kRowsPerGroup - 1) / mla::kRowsPerGroup;
+    if (params->num_workers > 0) {
+        h->num_workers = params->num_workers;
+    } else {
+        // one workgroup per compute unit (the kernel holds a CU's LDS); keep the
+        // row groups of one worker on one XCD by using a multiple of 8 workers
+        int w = h->compute_units / h->row_groups;
+        if (w >= 8) w = w / 8 * 8;
+        h->num_workers = w > 0 ? w : 1;
+    }
+    h->partial_slots = h->num_workers > 1 ? 2 * (h->num_workers - 1) : 1;
+    const char* log = std::getenv("MLA_DECODE_LOG");
+    if (log && log[0] == '1') {
+        std::fprintf(stderr, "[mla_decode] device %d (%s) CUs=%d rows=%d row_groups=%d workers=%d kv=%s\n",
+                     dev, prop.gcnArchName, h->compute_units, h->rows, h->row_groups, h->num_workers,
+                     params->kv_dtype == MLA_KV_BF16 ? "bf16" : "fp8");
+    }
+    *out = h;
+    return MLA_OK;
+}
+
+mla_status_t mla_decode_workspace_size(mla_decode_handle_t h, int32_t batch, size_t* bytes) {
+    if (!h || !bytes) return MLA_ERR_INVALID_ARGUMENT;
+    if (batch < 0 || batch > h->p.max_batch) return MLA_ERR_INVALID_ARGUMENT;
+    *bytes = layout(h, batch).total;
+    return MLA_OK;
+}
+
+mla_status_t mla_decode_set_profile_events(mla_decode_handle_t h, void* ev_start, void* ev_stop) {
+    if (!h) return MLA_ERR_INVALID_ARGUMENT;
+    if ((ev_start == nullptr) != (ev_stop == nullptr)) return MLA_ERR_INVALID_ARGUMENT;
+    h->ev_start = (hipEvent_t)ev_start;
+    h->ev_stop = (hipEvent_t)ev_stop;
+    return MLA_OK;
+}
+
+mla_status_t mla_decode_get_info(mla_decode_handle_t h, int32_t* num_workers, int32_t* row_groups,
+                                 int32_t* compute_units) {
+    if (!h) return MLA_ERR_INVALID_ARGUMENT;
+    if (num_workers) *num_workers = h->num_workers;
+    if (row_groups) *row_groups = h->row_groups;
+    if (compute_units) *compute_units = h->compute_units;
+    return MLA_OK;
+}
+
+mla_status_t mla_decode_free(mla_decode_handle_t h) {
+    delete h;
+    return MLA_OK;
+}
+
+mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv_pages,
+                            const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* hip_stream) {
+    if (!h) return MLA_ERR_INVALID_ARGUMENT;
+    if (batch < 0 || batch > h->p.max_batch) return MLA_ERR_INVALID_ARGUMENT;
+    if (batch == 0) return MLA_OK;
+    if (!q || !kv_pages || !block_table || !seq_lens || !out || !workspace) return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(out, 16)) return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, kAlign)) return MLA_ERR_INVALID_ARGUMENT;
+    const WsLayout l = layout(h, batch);
+    if (workspace_bytes < l.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+    uint8_t* ws = (uint8_t*)workspace;
+    mla::PlanView plan;
+    plan.header = (int32_t*)(ws + l.header);
+    plan.segs = (int4*)(ws + l.segs);
+    plan.seg_worker = (int32_t*)(ws + l.seg_worker);
+    plan.worker_start = (int32_t*)(ws + l.worker_start);
+    plan.seq_nsplit = (int32_t*)(ws + l.seq_nsplit);
+    plan.seq_slot = (int32_t*)(ws + l.seq_slot);
+    plan.part_lse = (float*)(ws + l.part_lse);
+    plan.part_o = (float*)(ws + l.part_o);
+    hipStream_t stream = (hipStream_t)hip_stream;
+
+    mla::PlanArgs pa;
+    pa.seq_lens = seq_lens;
+    pa.plan = plan;
+    pa.batch = batch;
+    pa.num_workers = h->num_workers;
+    pa.overhead_units = kOverheadUnits;
+    pa.min_quota = kMinQuota;
+    if (mla::launch_plan(pa, stream) != hipSuccess) return MLA_ERR_HIP;
+
+    mla::DecodeArgs da;
+    da.q = (const uint16_t*)q;
+    da.kv = (const uint8_t*)kv_pages;
+    da.block_table = block_table;
+    da.seq_lens = seq_lens;
+    da.out = out;
+    da.lse = lse;
+    da.plan = plan;
+    da.page_bytes = (int64_t)h->p.block_size *
+                    (int64_t)mla_kv_row_stride(h->p.kv_dtype, h->p.d_c, h->p.d_r);
+    da.batch = batch;
+    da.s_q = h->p.s_q;
+    da.n_h = h->p.n_h;
+    da.max_blocks = h->p.max_blocks_per_seq;
+    da.num_workers = h->num_workers;
+    da.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
+    if (h->ev_start && hipEventRecord(h->ev_start, stream) != hipSuccess) return MLA_ERR_HIP;
+    const hipError_t e = h->p.kv_dtype == MLA_KV_BF16 ? mla::launch_decode_bf16(da, h->row_groups, stream)
+                                                      : mla::launch_decode_fp8(da, h->row_groups, stream);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    if (h->ev_stop && hipEventRecord(h->ev_stop, stream) != hipSuccess) return MLA_ERR_HIP;
+
+    mla::CombineArgs ca;
+    ca.plan = plan;
+    ca.out = out;
+    ca.lse = lse;
+    ca.batch = batch;
+    ca.rows = h->rows;
+    if (mla::launch_combine(ca, stream) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+}  // extern "C"

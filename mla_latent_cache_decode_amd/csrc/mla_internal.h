@@ -1,0 +1,76 @@
+// Internal interface between the C-ABI host code (api.cpp) and the kernel
+// translation units.  Not installed; the public ABI is include/mla_decode.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Shapes this build instantiates (guide section 1.1: 512 latent + 64 RoPE;
+// "DeepSeek-R1" record, constraint (1): page block of 64 tokens).
+constexpr int kPage = 64;
+constexpr int kDc = 512;
+constexpr int kDr = 64;
+constexpr int kD = kDc + kDr;                 // 576 elements per cached row
+constexpr int kBf16RowBytes = 2 * kD;         // 1152
+constexpr int kFp8Payload = kD + kD / 32;     // 594
+constexpr int kFp8RowBytes = (kFp8Payload + 15) / 16 * 16;  // 608
+constexpr int kRowsPerGroup = 128;            // query rows one workgroup serves
+constexpr int kRowsPerWave = 32;
+constexpr int kDecodeThreads = 256;           // 4 waves of 64
+
+// Work plan written by the planner kernel into the workspace.
+struct PlanView {
+    int32_t* header;            // [0] quota (pages+overhead units per worker), [1] segments
+    int4* segs;                 // {b, page_lo, page_hi, partial slot or -1}
+    int32_t* seg_worker;        // worker id of each segment (non-decreasing)
+    int32_t* worker_start;      // [num_workers + 1] first segment of each worker
+    int32_t* seq_nsplit;        // [batch] segments per sequence
+    int32_t* seq_slot;          // [batch] first partial slot of the sequence
+    float* part_lse;            // [slots][M]
+    float* part_o;              // [slots][M][kDc]
+};
+
+struct DecodeArgs {
+    const uint16_t* q;          // bf16 [B][s_q][n_h][kD]
+    const uint8_t* kv;          // pages
+    const int32_t* block_table; // [B][max_blocks]
+    const int32_t* seq_lens;    // [B]
+    float* out;                 // [B][M][kDc]
+    float* lse;                 // [B][M] or null
+    PlanView plan;
+    int64_t page_bytes;         // bytes per page
+    int32_t batch;
+    int32_t s_q;
+    int32_t n_h;
+    int32_t max_blocks;
+    int32_t num_workers;
+    float scale_log2;           // softmax_scale * log2(e)
+};
+
+struct PlanArgs {
+    const int32_t* seq_lens;
+    PlanView plan;
+    int32_t batch;
+    int32_t num_workers;
+    int32_t overhead_units;     // per-segment fixed cost, in pages
+    int32_t min_quota;          // lower bound on pages per worker
+};
+
+struct CombineArgs {
+    PlanView plan;
+    float* out;
+    float* lse;                 // may be null
+    int32_t batch;
+    int32_t rows;               // M = s_q * n_h
+};
+
+// Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,171 @@
+"""GPU parity: the HIP decode (through the C ABI) against the float64 oracle on
+the same seeded bytes.  Element-by-element at reduced sizes that still span
+several pages, splits and ragged tails; on sampled sequences at the full
+workload sizes, in the launch configuration the bench times."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from mla_inputs import SPECS, WorkloadSpec, make_workload, to_torch
+from gpu_helpers import run_gpu, oracle, assert_parity, make_decoder, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["single_1k_small", "paged_b32_small", "long_ctx_b4_small", "fp8_b64_small", "mtp2_b128_small"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_parity_small_all_elements(name):
+    w = make_workload(name)
+    out, lse = run_gpu(w)
+    ro, rl = oracle(w)
+    assert_parity(w, out, lse, ro, rl)
+
+
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("workers", [1, 3, 16, 300])
+def test_parity_small_any_split(name, workers):
+    # forcing the number of context splits exercises the planner and combine
+    w = make_workload(name)
+    out, lse = run_gpu(w, num_workers=workers)
+    ro, rl = oracle(w)
+    assert_parity(w, out, lse, ro, rl)
+
+
+FULL_SAMPLES = {
+    "single_1k": None,
+    "paged_b32": [0, 7, 31],
+    "long_ctx_b4": [0, 2],
+    "fp8_b64": [0, 33, 63],
+    "mtp2_b128": [0, 64, 127],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
+def test_parity_full_size_sampled(name):
+    w = make_workload(name)
+    batches = FULL_SAMPLES[name]
+    if batches is None:
+        batches = list(range(w.spec.batch))
+    # include the longest sequence
+    batches = sorted(set(batches) | {int(np.argmax(w.seq_lens))})
+    out, lse = run_gpu(w)
+    ro, rl = oracle(w, batches=batches)
+    assert_parity(w, out, lse, ro, rl, batches=batches)
+    # every output of every sequence is finite and every lse is finite
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def _identity_layout(w):
+    """Same logical cache, pages stored in logical order (identity block table)."""
+    pages = (w.seq_lens.astype(np.int64) + 63) // 64
+    rows = [w.block_table[b, :pages[b]] for b in range(w.spec.batch)]
+    order = np.concatenate(rows)
+    pool2 = w.pool[order].copy()
+    bt2 = np.full_like(w.block_table, -1)
+    off = 0
+    for b in range(w.spec.batch):
+        bt2[b, :pages[b]] = np.arange(off, off + pages[b])
+        off += pages[b]
+    return dataclasses.replace(w, pool=pool2, block_table=bt2)
+
+
+@pytest.mark.parametrize("name", ["paged_b32_small", "fp8_b64_small", "mtp2_b128_small"])
+def test_paged_equals_identity_bitwise(name):
+    w = make_workload(name)
+    w2 = _identity_layout(w)
+    o1, l1 = run_gpu(w, num_workers=7)
+    o2, l2 = run_gpu(w2, num_workers=7)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["long_ctx_b4_small", "fp8_b64_small"])
+def test_repeat_runs_bitwise_identical(name):
+    w = make_workload(name)
+    t = to_torch(w, torch.device("cuda:0"))
+    dec = make_decoder(w)
+    o1, l1 = run_gpu(w, tensors=t, dec=dec)
+    o2, l2 = run_gpu(w, tensors=t, dec=dec)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["paged_b32_small", "fp8_b64_small"])
+def test_unread_bytes_do_not_matter(name):
+    # rewrite every byte the decode must not read (tails, spare pages, padding)
+    w = make_workload(name)
+    pages = (w.seq_lens.astype(np.int64) + 63) // 64
+    used = np.zeros(w.pool.shape[:2], dtype=bool)
+    for b in range(w.spec.batch):
+        for t in range(int(w.seq_lens[b])):
+            used[w.block_table[b, t // 64], t % 64] = True
+    pool2 = w.pool.copy()
+    pool2[~used] = 0x5A5A if w.spec.kv_dtype == "bf16" else 0xFF
+    if w.spec.kv_dtype == "fp8":
+        pool2[:, :, 594:] = 0x7F
+    w2 = dataclasses.replace(w, pool=pool2)
+    o1, l1 = run_gpu(w, num_workers=5)
+    o2, l2 = run_gpu(w2, num_workers=5)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+EDGE = [
+    # one token, a page multiple, one past a page, causal s_q=2 with L = 1 (query 0 sees nothing)
+    WorkloadSpec("edge_lens", 6, ("fixed", (1, 64, 65, 128, 129, 3)), spare_pages=4, seed=11),
+    WorkloadSpec("edge_mtp", 5, ("fixed", (1, 2, 64, 65, 200)), s_q=2, spare_pages=4, seed=12),
+    WorkloadSpec("edge_fp8", 4, ("fixed", (1, 63, 64, 700)), kv_dtype="fp8", spare_pages=4, seed=13,
+                 outlier_p=0.01, outlier_mult=20.0),
+    WorkloadSpec("edge_heads32", 3, ("fixed", (100, 5, 300)), n_h=32, spare_pages=2, seed=14),
+    WorkloadSpec("edge_heads64_mtp", 3, ("fixed", (100, 5, 300)), n_h=64, s_q=2, spare_pages=2, seed=15),
+    WorkloadSpec("edge_heads256", 2, ("fixed", (129, 640)), n_h=256, spare_pages=2, seed=16),
+    WorkloadSpec("edge_mtp4", 3, ("fixed", (3, 66, 257)), s_q=4, spare_pages=2, seed=17),
+    WorkloadSpec("edge_empty_seq", 3, ("fixed", (0, 70, 0)), spare_pages=2, seed=18),
+]
+
+
+@pytest.mark.parametrize("spec", EDGE, ids=[s.name for s in EDGE])
+@pytest.mark.parametrize("workers", [0, 2])
+def test_edge_cases(spec, workers):
+    w = make_workload(spec)
+    out, lse = run_gpu(w, num_workers=workers)
+    ro, rl = oracle(w)
+    assert_parity(w, out, lse, ro, rl)
+
+
+def test_without_lse_output():
+    w = make_workload("paged_b32_small")
+    out, _ = run_gpu(w, with_lse=False)
+    ro, rl = oracle(w)
+    assert_parity(w, out, None, ro, rl)
+
+
+def test_batch_zero_is_a_noop_and_errors_are_reported():
+    import mla_latent_cache_decode_amd as m
+    w = make_workload("paged_b32_small")
+    dec = make_decoder(w)
+    t = to_torch(w, torch.device("cuda:0"))
+    lib = m.load_library()
+    ws = dec.alloc_workspace(w.spec.batch)
+    out = torch.zeros((w.spec.batch, 1, 128, 512), dtype=torch.float32, device="cuda")
+    say("error paths")
+    assert lib.mla_decode_run(dec._h, t["q"].data_ptr(), t["kv"].data_ptr(), t["block_table"].data_ptr(),
+                              t["seq_lens"].data_ptr(), 0, out.data_ptr(), None, ws.data_ptr(), 0, None) == 0
+    # workspace too small
+    assert lib.mla_decode_run(dec._h, t["q"].data_ptr(), t["kv"].data_ptr(), t["block_table"].data_ptr(),
+                              t["seq_lens"].data_ptr(), w.spec.batch, out.data_ptr(), None, ws.data_ptr(),
+                              16, None) == m.MLA_ERR_WORKSPACE_TOO_SMALL
+    # misaligned output
+    assert lib.mla_decode_run(dec._h, t["q"].data_ptr(), t["kv"].data_ptr(), t["block_table"].data_ptr(),
+                              t["seq_lens"].data_ptr(), w.spec.batch, out.data_ptr() + 4, None, ws.data_ptr(),
+                              ws.numel(), None) == m.MLA_ERR_INVALID_ARGUMENT
+    # batch above max_batch
+    assert lib.mla_decode_run(dec._h, t["q"].data_ptr(), t["kv"].data_ptr(), t["block_table"].data_ptr(),
+                              t["seq_lens"].data_ptr(), w.spec.batch + 1, out.data_ptr(), None, ws.data_ptr(),
+                              ws.numel(), None) == m.MLA_ERR_INVALID_ARGUMENT
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
