@@ -25,20 +25,34 @@
 //    16-byte chunk c sits at slot t*8 + (c ^ sw(t)).  The swizzle keeps the
 //    row-wise 128-bit reads of Q.K^T and the transposed 64-bit reads of the
 //    PV operand (ds_read_b64_tr_b16) free of bank conflicts.
+//  * Both products run as fp16 MFMA with fp32 accumulation.  A landed bf16
+//    page is converted to fp16 in place, once per workgroup (exact for
+//    values inside the fp16 range: bf16 carries fewer significand bits).
+//    fp16 matters for P: its rounding error is 8x below bf16's, which keeps
+//    the softmax weights accurate even when the reference max is stale.
 //  * Lazy rescaling: the running max is only raised when a tile's max
-//    exceeds it by more than 2^8, so O is almost never rescaled after the
-//    first tile; exponentials stay <= 2^8, far inside fp32/bf16 range.
+//    exceeds it by more than 2^15 (in exp2 units), so O is rarely rescaled
+//    after the first tile; exponentials stay <= 2^15, inside fp16 range.
+//  * Queries are scaled per head by a power of two into [2^14, 2^15) before
+//    the fp16 conversion (exact), and the factor is folded into that head's
+//    softmax scale, so any query magnitude is representable.
 //  * FP8 pages (e4m3 codes + e8m0 per 32) land in an LDS staging buffer and
-//    are dequantised once per workgroup into the same bf16 tile layout
-//    (exact: an e4m3 value times a power of two is a bf16 value).
+//    are dequantised once per workgroup into the same fp16 tile layout
+//    (exact for values inside the fp16 range).
 #include "mla_internal.h"
+
+#include <type_traits>
+#include <utility>
 
 namespace mla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x4_tr __attribute__((__vector_size__(4 * sizeof(__fp16))));   // tr-read builtin type
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -53,7 +67,7 @@ constexpr int kMdBlocks = kDc / 32;             // 16 output blocks of 32 dims
 constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;   // 18 direct-to-LDS loads
 constexpr int kFp8StageBytes = kPage * kFp8RowBytes;   // 38912
 constexpr int kFp8Loads = kFp8StageBytes / 1024;       // 38
-constexpr float kRescaleTau = 8.0f;             // log2 units
+constexpr float kRescaleTau = 15.0f;            // log2 units: p <= 2^15 stays inside fp16
 
 constexpr int kLdsBf16 = 2 * kTileBytes;                        // 147456
 constexpr int kLdsFp8 = kTileBytes + 2 * kFp8StageBytes;        // 151552
@@ -75,9 +89,17 @@ __device__ __forceinline__ T ld_const(const T* p) {
     return *(const CONST_AS T*)p;
 }
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
 __device__ __forceinline__ int sw(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
-// byte offset of (token t, chunk c) inside a bf16 tile
+// byte offset of (token t, chunk c) inside a tile (16-bit elements)
 __device__ __forceinline__ int tile_off(int t, int c) {
     return (((c >> 3) << 9) + (t << 3) + ((c & 7) ^ sw(t))) << 4;
 }
@@ -188,11 +210,12 @@ __device__ __forceinline__ void load_page_fp8(const uint8_t* page, LDS_AS uint8_
 }
 
 __device__ __forceinline__ float e8m0_to_float(uint32_t e) {
+    // 2^(e-127); e = 0 is the fp32 subnormal 2^-127, e = 255 is NaN
     uint32_t bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : (e << 23));
     return __builtin_bit_cast(float, bits);
 }
 
-// Dequantise a staged fp8 page into the bf16 tile (all 256 threads).
+// Dequantise a staged fp8 page into the fp16 tile (all 256 threads).
 __device__ __forceinline__ void convert_fp8_page(const LDS_AS uint8_t* stage, LDS_AS uint8_t* tile,
                                                  int tid) {
 #pragma unroll 6
@@ -203,12 +226,31 @@ __device__ __forceinline__ void convert_fp8_page(const LDS_AS uint8_t* stage, LD
         const LDS_AS uint8_t* row = stage + t * kFp8RowBytes;
         const u32x2 codes = *(const LDS_AS u32x2*)(row + c * 8);
         const float scale = e8m0_to_float(row[kD + (c >> 2)]);
-        bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], scale, false);
-        bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], scale, true);
-        bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], scale, false);
-        bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], scale, true);
-        bf16x8 v = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        *(LDS_AS bf16x8*)(tile + tile_off(t, c)) = v;
+        f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[0], scale, false);
+        f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[0], scale, true);
+        f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[1], scale, false);
+        f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[1], scale, true);
+        f16x8 v = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        *(LDS_AS f16x8*)(tile + tile_off(t, c)) = v;
+    }
+}
+
+// Convert a landed bf16 tile to fp16 in place (all 256 threads, 18 chunks
+// of 16 bytes each; a chunk is read and written by the same thread).
+__device__ __forceinline__ void convert_bf16_tile(LDS_AS uint8_t* tile, int tid) {
+#pragma unroll 6
+    for (int k = 0; k < kTileBytes / 16 / kDecodeThreads; ++k) {
+        LDS_AS u32x4* p = (LDS_AS u32x4*)(tile + (tid + kDecodeThreads * k) * 16);
+        const u32x4 v = *p;
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = __builtin_bit_cast(float, v[i] << 16);
+            const float hi = __builtin_bit_cast(float, v[i] & 0xFFFF0000u);
+            const f16x2 h = {(_Float16)lo, (_Float16)hi};
+            r[i] = __builtin_bit_cast(uint32_t, h);
+        }
+        *p = r;
     }
 }
 
@@ -221,6 +263,16 @@ struct WaveState {
     float l;                 // partial sum of exp over this lane's half of the tokens
     bool o_zero;             // nothing accumulated yet (wave-uniform)
 };
+
+// The lane id, hidden from loop-invariant code motion.  Lane-derived
+// offsets are recomputed from it per tile (a handful of VALU ops) instead of
+// being hoisted out of the page loop, where they would occupy registers for
+// the whole kernel and push the register allocator into spilling.
+__device__ __forceinline__ int opaque_lane() {
+    int l = __lane_id();
+    asm volatile("" : "+v"(l));
+    return l;
+}
 
 // Lane-constant byte offsets into a tile (see tile_off):
 //   k_off[k]  Q.K^T A-operand: token (lane & 31), chunk 2*ks + (lane >> 5) for
@@ -248,9 +300,10 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
     return o;
 }
 
-__device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const bf16x8 (&qf)[kKSteps],
-                                             WaveState& st, const LaneOffsets& lo, int lane, int n_valid,
-                                             float scale_log2) {
+__device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f16x8 (&qf)[kKSteps],
+                                             WaveState& st, int n_valid, float scale_log2) {
+    const int lane = opaque_lane();
+    const LaneOffsets lo = lane_offsets(lane);
     const int hi = lane >> 5;
     const LDS_AS uint8_t* kp[4];
 #pragma unroll
@@ -260,18 +313,18 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const b
     // ahead; the scheduling groups keep that order so at most two k-steps of
     // fragments are live (the scheduler would otherwise hoist every read).
     f32x16 s0 = {}, s1 = {};
-    bf16x8 ka[2], kb[2];
-    ka[0] = *(const LDS_AS bf16x8*)(kp[0]);
-    kb[0] = *(const LDS_AS bf16x8*)(kp[0] + 4096);
+    f16x8 ka[2], kb[2];
+    ka[0] = *(const LDS_AS f16x8*)(kp[0]);
+    kb[0] = *(const LDS_AS f16x8*)(kp[0] + 4096);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
         if (ks + 1 < kKSteps) {
             const LDS_AS uint8_t* base = kp[(ks + 1) & 3] + ((ks + 1) >> 2) * 8192;
-            ka[(ks + 1) & 1] = *(const LDS_AS bf16x8*)(base);
-            kb[(ks + 1) & 1] = *(const LDS_AS bf16x8*)(base + 4096);
+            ka[(ks + 1) & 1] = *(const LDS_AS f16x8*)(base);
+            kb[(ks + 1) & 1] = *(const LDS_AS f16x8*)(base + 4096);
         }
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1], qf[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[ks & 1], qf[ks], s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks & 1], qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kb[ks & 1], qf[ks], s1, 0, 0, 0);
         if (ks + 1 < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                          // 2 MFMA
     }
@@ -320,37 +373,53 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const b
         lsum += p0 + p1;
     }
     st.l += lsum;
-    bf16x8 pf[4];
+    f16x8 pf[4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        pf[0][e] = (__bf16)s0[e];
-        pf[1][e] = (__bf16)s0[8 + e];
-        pf[2][e] = (__bf16)s1[e];
-        pf[3][e] = (__bf16)s1[8 + e];
+        pf[0][e] = (_Float16)s0[e];
+        pf[1][e] = (_Float16)s0[8 + e];
+        pf[2][e] = (_Float16)s1[e];
+        pf[3][e] = (_Float16)s1[8 + e];
     }
 
     // O^T += V^T P^T ; V^T fragments through transposed LDS reads, one
-    // (kb, md) step ahead of their MFMA.
+    // (kb, md) step ahead of their MFMA.  The reads are issued as asm: the
+    // compiler cannot tell that they do not alias the page prefetch still
+    // in flight and would otherwise wait for it (vmcnt(0)) here.  The
+    // lgkmcnt wait is tied to the fragment registers so the MFMA cannot be
+    // scheduled above it.
     __builtin_amdgcn_sched_barrier(0);
-    const LDS_AS uint8_t* vp0 = tile + lo.v_off[0];
-    const LDS_AS uint8_t* vp1 = tile + lo.v_off[1];
-    auto read_v = [&](int step) -> bf16x8 {
-        const int kb_ = step >> 4, md = step & 15;
-        const LDS_AS uint8_t* vb = ((md & 1) ? vp1 : vp0) + (md >> 1) * 8192 + kb_ * 16 * 128;
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + 8 * 128));
-        return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    const uint32_t vp0 = (uint32_t)(uintptr_t)(tile + lo.v_off[0]);
+    const uint32_t vp1 = (uint32_t)(uintptr_t)(tile + lo.v_off[1]);
+    // three rotating fragment buffers: a read never targets the registers of
+    // the MFMA issued just before it (no write-after-read on its operands)
+    f16x8 vf[3];
+    auto read_v = [&](auto step_c) -> f16x8 {
+        constexpr int step = decltype(step_c)::value;
+        constexpr int kb_ = step >> 4, md = step & 15;
+        constexpr int off = (md >> 1) * 8192 + kb_ * 16 * 128;
+        f16x4 v0, v1;
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v0) : "v"((md & 1) ? vp1 : vp0), "i"(off));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                     : "=v"(v1)
+                     : "v"((md & 1) ? vp1 : vp0), "i"(off + 8 * 128));
+        return f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     };
-    bf16x8 vf[2];
-    vf[0] = read_v(0);
-#pragma unroll
-    for (int step = 0; step < 4 * kMdBlocks; ++step) {
-        if (step + 1 < 4 * kMdBlocks) vf[(step + 1) & 1] = read_v(step + 1);
-        st.o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[step & 1], pf[step >> 4], st.o[step & 15],
-                                                                   0, 0, 0);
-        if (step + 1 < 4 * kMdBlocks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
+    vf[0] = read_v(std::integral_constant<int, 0>{});
+    static_for<0, 4 * kMdBlocks>([&](auto step_c) {
+        constexpr int step = decltype(step_c)::value;
+        if constexpr (step + 1 < 4 * kMdBlocks) {
+            vf[(step + 1) % 3] = read_v(std::integral_constant<int, step + 1>{});
+            // the previous MFMA's operand stays allocated across this read
+            if constexpr (step > 0) asm volatile("" ::"v"(vf[(step + 2) % 3]));
+            asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(vf[step % 3]));
+        } else {
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(vf[step % 3]));
+        }
+        st.o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[step % 3], pf[step >> 4], st.o[step & 15],
+                                                                  0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);     // keep [read s+1, wait, mfma s] in order
+    });
     __builtin_amdgcn_sched_barrier(0);
     // keep the accumulator's home in AGPRs (it is only touched by MFMA in the
     // steady state); VALU users copy out and back
@@ -393,11 +462,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
     }
     __syncthreads();
 
-    const LaneOffsets lofs = lane_offsets(lane);
-    const int ld_tok = lane >> 3;                                   // bf16 loader lane constant
-    const int ld_off = ld_tok * kBf16RowBytes + (((lane & 7) ^ sw(ld_tok)) << 4);
 
-    LDS_AS uint8_t* tile_c = lds;                          // fp8: the single bf16 tile
+    LDS_AS uint8_t* tile_c = lds;                          // fp8: the single fp16 tile
     LDS_AS uint8_t* bufs[2];
     if (kFp8) {
         bufs[0] = lds + kTileBytes;
@@ -423,12 +489,21 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         };
         auto issue = [&](int p, LDS_AS uint8_t* dst) {
             const int nv = min(max(n_load - p * kPage, 0), kPage);
-            if (kFp8) load_page_fp8(page_ptr(p), dst, wave, lane, nv);
-            else load_page_bf16(page_ptr(p), dst, wave, ld_off, nv);
+            const int ol = opaque_lane();
+            if (kFp8) {
+                load_page_fp8(page_ptr(p), dst, wave, ol, nv);
+            } else {
+                const int ld_tok = ol >> 3;                       // bf16 loader lane offset
+                load_page_bf16(page_ptr(p), dst, wave, ld_tok * kBf16RowBytes + (((ol & 7) ^ sw(ld_tok)) << 4), nv);
+            }
         };
 
-        // this wave's 32 query rows as MFMA B operands (q_abs || q_R, bf16)
-        bf16x8 qf[kKSteps];
+        // this wave's 32 query rows as MFMA B operands (q_abs || q_R): bf16
+        // loaded, scaled per head by 2^-a so the head's max |q| lands in
+        // [2^14, 2^15), converted to fp16 (exact up to fp16 subnormals); the
+        // head's softmax scale absorbs 2^a
+        f16x8 qf[kKSteps];
+        float scale_lane;
         WaveState st;
         st.m = -__builtin_inff();
         st.l = 0.f;
@@ -438,8 +513,27 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         {
             const int row = active ? row0 + (lane & 31) : 0;
             const uint16_t* qrow = a.q + ((int64_t)b * M + row) * kD + (lane >> 5) * 8;
+            float qmax = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8*)(qrow + ks * 16);
+            for (int ks = 0; ks < kKSteps; ++ks) {
+                const bf16x8 qb = *(const bf16x8*)(qrow + ks * 16);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf((float)qb[e]));
+                qf[ks] = __builtin_bit_cast(f16x8, qb);          // raw bits for now
+            }
+            qmax = pair_max(qmax);
+            // exponent of qmax (a normal or zero float after the bf16 widening)
+            const int ex = qmax > 0.f ? (int)((__builtin_bit_cast(uint32_t, qmax) >> 23) & 0xFF) - 127 : 14;
+            const int sh = ex - 14;
+            const float down = __builtin_bit_cast(float, (uint32_t)(127 - sh) << 23);   // 2^-sh
+            const float up = __builtin_bit_cast(float, (uint32_t)(127 + sh) << 23);     // 2^sh
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) {
+                const bf16x8 qb = __builtin_bit_cast(bf16x8, qf[ks]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)((float)qb[e] * down);
+            }
+            scale_lane = a.scale_log2 * up;
         }
 
         // prefetch the first two pages of the segment (after the query loads,
@@ -465,19 +559,22 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
 
             const LDS_AS uint8_t* tile;
             if (kFp8) {
-                convert_fp8_page(bufs[sb], tile_c, tid);
+                convert_fp8_page(bufs[sb], tile_c, wave * 64 + opaque_lane());
                 __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): LDS writes done
                 wg_barrier();
                 if (p + 2 < p_hi) issue(p + 2, bufs[sb]);
                 tile = tile_c;
             } else {
+                convert_bf16_tile(bufs[sb], wave * 64 + opaque_lane());
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                wg_barrier();
                 tile = bufs[sb];
             }
 
             // inactive waves (rows beyond M) compute on row 0's query and
             // discard the result: keeping the call unconditional keeps the
             // accumulators out of control-flow merges
-            compute_tile(tile, qf, st, lofs, lane, min(max(n_vis - p * kPage, 0), kPage), a.scale_log2);
+            compute_tile(tile, qf, st, min(max(n_vis - p * kPage, 0), kPage), scale_lane);
 
             if (!kFp8) {
                 __builtin_amdgcn_s_waitcnt(0xC07F);       // this wave's LDS reads retired
