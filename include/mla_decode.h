@@ -78,7 +78,7 @@ typedef struct mla_decode_params {
     float   softmax_scale;      /* multiplies q.row; finite and > 0 (e.g. 1/sqrt(192))      */
     int32_t num_workers;        /* 0 = one worker per compute unit (chosen at init);
                                    > 0 forces that many context-split workers (tests,
-                                   sweeps); at most 65536                                   */
+                                   sweeps); at most 4096                                   */
     int32_t flags;              /* MLA_FLAG_*                                               */
 } mla_decode_params_t;
 

@@ -1,9 +1,10 @@
 // C ABI of the MLA decode library (declared in include/mla_decode.h).
 //
 // Host responsibilities: validate every argument before touching HIP, query
-// the device once at init, size the workspace, and enqueue planner -> decode
-// -> combine on the caller's stream without synchronising.  All device
-// memory is the caller's.
+// the device once at init, size the workspace, and enqueue decode -> combine
+// on the caller's stream without synchronising (the work plan is derived
+// from seq_lens on the device, inside the decode kernel).  All device memory
+// is the caller's.
 #include "mla_decode.h"
 
 #include <hip/hip_runtime.h>
@@ -37,19 +38,15 @@ constexpr int kMinQuota = 1;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-    size_t header, segs, seg_worker, worker_start, seq_nsplit, seq_slot, part_lse, part_o, total;
+    size_t seq_nsplit, seq_slot, part_lse, part_o, total;
 };
 
 WsLayout layout(const mla_decode_handle* h, int32_t batch) {
     WsLayout l{};
-    const size_t nseg = (size_t)h->num_workers + (size_t)batch;
+    const size_t nb = (size_t)(batch > 0 ? batch : 1);
     size_t off = 0;
-    l.header = off;        off += align_up(16 * sizeof(int32_t));
-    l.segs = off;          off += align_up(nseg * sizeof(int4));
-    l.seg_worker = off;    off += align_up(nseg * sizeof(int32_t));
-    l.worker_start = off;  off += align_up(((size_t)h->num_workers + 1) * sizeof(int32_t));
-    l.seq_nsplit = off;    off += align_up((size_t)(batch > 0 ? batch : 1) * sizeof(int32_t));
-    l.seq_slot = off;      off += align_up((size_t)(batch > 0 ? batch : 1) * sizeof(int32_t));
+    l.seq_nsplit = off;    off += align_up(nb * sizeof(int32_t));
+    l.seq_slot = off;      off += align_up(nb * sizeof(int32_t));
     l.part_lse = off;      off += align_up((size_t)h->partial_slots * h->rows * sizeof(float));
     l.part_o = off;        off += align_up((size_t)h->partial_slots * h->rows * mla::kDc * sizeof(float));
     l.total = off;
@@ -68,7 +65,7 @@ mla_status_t validate_params(const mla_decode_params_t* p) {
     if ((int64_t)p->max_blocks_per_seq * p->block_size > (int64_t)1 << 30) return MLA_ERR_INVALID_ARGUMENT;
     if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3_E8M0) return MLA_ERR_INVALID_ARGUMENT;
     if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
-    if (p->num_workers < 0 || p->num_workers > 65536) return MLA_ERR_INVALID_ARGUMENT;
+    if (p->num_workers < 0 || p->num_workers > mla::kMaxWorkers) return MLA_ERR_INVALID_ARGUMENT;
     if (p->flags != MLA_FLAG_NONE) return MLA_ERR_INVALID_ARGUMENT;
     if ((p->d_c + p->d_r) % 32 != 0 && p->kv_dtype == MLA_KV_FP8_E4M3_E8M0) return MLA_ERR_INVALID_ARGUMENT;
     // valid requests outside what this build instantiates
@@ -135,7 +132,7 @@ mla_status_t mla_decode_init(const mla_decode_params_t* params, mla_decode_handl
         // row groups of one worker on one XCD by using a multiple of 8 workers
         int w = h->compute_units / h->row_groups;
         if (w >= 8) w = w / 8 * 8;
-        h->num_workers = w > 0 ? w : 1;
+        h->num_workers = w < 1 ? 1 : (w > mla::kMaxWorkers ? mla::kMaxWorkers : w);
     }
     h->partial_slots = h->num_workers > 1 ? 2 * (h->num_workers - 1) : 1;
     const char* log = std::getenv("MLA_DECODE_LOG");
@@ -194,24 +191,11 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
 
     uint8_t* ws = (uint8_t*)workspace;
     mla::PlanView plan;
-    plan.header = (int32_t*)(ws + l.header);
-    plan.segs = (int4*)(ws + l.segs);
-    plan.seg_worker = (int32_t*)(ws + l.seg_worker);
-    plan.worker_start = (int32_t*)(ws + l.worker_start);
     plan.seq_nsplit = (int32_t*)(ws + l.seq_nsplit);
     plan.seq_slot = (int32_t*)(ws + l.seq_slot);
     plan.part_lse = (float*)(ws + l.part_lse);
     plan.part_o = (float*)(ws + l.part_o);
     hipStream_t stream = (hipStream_t)hip_stream;
-
-    mla::PlanArgs pa;
-    pa.seq_lens = seq_lens;
-    pa.plan = plan;
-    pa.batch = batch;
-    pa.num_workers = h->num_workers;
-    pa.overhead_units = kOverheadUnits;
-    pa.min_quota = kMinQuota;
-    if (mla::launch_plan(pa, stream) != hipSuccess) return MLA_ERR_HIP;
 
     mla::DecodeArgs da;
     da.q = (const uint16_t*)q;
@@ -228,6 +212,8 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     da.n_h = h->p.n_h;
     da.max_blocks = h->p.max_blocks_per_seq;
     da.num_workers = h->num_workers;
+    da.overhead_units = kOverheadUnits;
+    da.min_quota = kMinQuota;
     da.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
     if (h->ev_start && hipEventRecord(h->ev_start, stream) != hipSuccess) return MLA_ERR_HIP;
     const hipError_t e = h->p.kv_dtype == MLA_KV_BF16 ? mla::launch_decode_bf16(da, h->row_groups, stream)

@@ -21,14 +21,15 @@ constexpr int kRowsPerGroup = 128;            // query rows one workgroup serves
 constexpr int kRowsPerWave = 32;
 constexpr int kDecodeThreads = 256;           // 4 waves of 64
 
-// Work plan written by the planner kernel into the workspace.
+constexpr int kMaxWorkers = 4096;             // bound on context-split workers
+constexpr int kMaxSplits = kMaxWorkers;       // a sequence has at most one split per worker
+
+// Per-call scratch in the workspace.  The decode kernel writes, per
+// sequence, its number of splits and first partial slot; split partials
+// (O/l and lse) live in slots [slot, slot + nsplit).
 struct PlanView {
-    int32_t* header;            // [0] quota (pages+overhead units per worker), [1] segments
-    int4* segs;                 // {b, page_lo, page_hi, partial slot or -1}
-    int32_t* seg_worker;        // worker id of each segment (non-decreasing)
-    int32_t* worker_start;      // [num_workers + 1] first segment of each worker
-    int32_t* seq_nsplit;        // [batch] segments per sequence
-    int32_t* seq_slot;          // [batch] first partial slot of the sequence
+    int32_t* seq_nsplit;        // [batch]
+    int32_t* seq_slot;          // [batch]
     float* part_lse;            // [slots][M]
     float* part_o;              // [slots][M][kDc]
 };
@@ -47,16 +48,9 @@ struct DecodeArgs {
     int32_t n_h;
     int32_t max_blocks;
     int32_t num_workers;
+    int32_t overhead_units;     // per-segment fixed cost on the cost axis, in pages
+    int32_t min_quota;          // lower bound on cost units per worker
     float scale_log2;           // softmax_scale * log2(e)
-};
-
-struct PlanArgs {
-    const int32_t* seq_lens;
-    PlanView plan;
-    int32_t batch;
-    int32_t num_workers;
-    int32_t overhead_units;     // per-segment fixed cost, in pages
-    int32_t min_quota;          // lower bound on pages per worker
 };
 
 struct CombineArgs {
@@ -68,7 +62,6 @@ struct CombineArgs {
 };
 
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
-hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
