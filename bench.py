@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """MLA latent-cache decode throughput on one MI355X.
 
-One step = one call of the whole hot path (work planner, split-KV decode,
-LSE combine) over one batch of the long-context workload: batch 4, seq_lens
+One step = one call of the whole hot path (split-KV decode with its fused
+work plan, then the LSE combine) over one batch of the long-context
+workload: batch 4, seq_lens
 {32768, 65536, 131072, 131072}, n_h 128, d_c 512, d_R 64, bf16 paged cache
 (block 64, permuted pages).  Inputs are seeded synthetic data already
 resident in HBM before the timed region.
@@ -38,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: the long-context one)")
     ap.add_argument("--num-workers", type=int, default=0)
-    ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="oracle sample budget (seconds)")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0, help="oracle sample budget (seconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
@@ -55,9 +56,10 @@ def flops_per_step(w) -> int:
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
-    """The float64 oracle as it stands, on whole sequences of the same workload
-    until the time budget is used (always at least one sequence)."""
-    import numpy as np
+    """The float64 oracle as it stands, on the same workload: whole sequences in
+    batch order, wrapping around to repeat the batch, until the time budget is
+    used (always at least one sequence).  Rate = KV bytes of the sequences
+    processed over the wall time."""
     from oracle import mla_decode_ref
     try:
         from threadpoolctl import threadpool_info
@@ -66,19 +68,32 @@ def cpu_baseline(w, budget_s: float) -> dict:
         threads = os.cpu_count() or 1
     s = w.spec
     row_bytes = 2 * s.d if s.kv_dtype == "bf16" else s.d + s.d // 32
-    done, nbytes = [], 0
+    n_seq, tokens, nbytes = 0, 0, 0
     t0 = time.perf_counter()
-    for b in range(s.batch):
+    while True:
+        b = n_seq % s.batch
         mla_decode_ref(w.q_bits, w.pool, w.block_table, w.seq_lens, kv_dtype=s.kv_dtype, d_c=s.d_c,
                        d_r=s.d_r, page=s.page, softmax_scale=s.softmax_scale, batches=[b])
-        done.append(b)
+        n_seq += 1
+        tokens += int(w.seq_lens[b])
         nbytes += int(w.seq_lens[b]) * row_bytes
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"sequences {done} of {s.name} (all {s.n_h} heads, {sum(int(w.seq_lens[b]) for b in done)} "
-                      f"tokens), float64 numpy oracle, {dt:.2f} s"}
+            "sample": f"{n_seq} sequences of {s.name} taken in batch order, repeating the batch "
+                      f"({n_seq / s.batch:.2f} passes; {tokens} tokens, all {s.n_h} heads, s_q={s.s_q}), "
+                      f"float64 numpy oracle, {dt:.2f} s wall"}
+
+
+def measured_traffic(workload: str) -> dict | None:
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    if it was taken on this workload and on the kernel source as it is now."""
+    from mla_latent_cache_decode_amd.rocprof_summary import kernel_source_hash, read_traffic
+    t = read_traffic(os.path.join(ROOT, "profiles", f"mla_decode_kernel_{workload}_traffic.txt"))
+    if t is None or t["source_hash"] != kernel_source_hash():
+        return None
+    return t
 
 
 def main():
@@ -156,6 +171,7 @@ def main():
     tflops = fl / (ms_step * 1e-3) / 1e12
     k_gbs = kv_bytes / (kms * 1e-3) / 1e9
     info = dec.info()
+    traffic = measured_traffic(s.name)
     res = {
         "metric": "MLA decode KV-read GB/s (% of HBM peak) + TFLOP/s, n_h=128, 1 GPU",
         "value": round(gbs, 2),
@@ -179,7 +195,8 @@ def main():
         "tflop_s": round(tflops, 2),
         "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic["bytes_per_launch"] if traffic else None,
                      "kernel": "mla_decode_kernel", "kernel_ms": round(kms, 5),
                      "bytes_per_launch": kv_bytes},
     }

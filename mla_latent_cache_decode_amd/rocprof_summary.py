@@ -1,0 +1,143 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept in profiles/.
+
+Two modes:
+
+  stats    from a ``rocprofv3 --kernel-trace --stats --output-format csv`` run:
+           per-kernel call count and average / min / max duration.
+  traffic  from two ``rocprofv3 --pmc`` runs (FETCH_SIZE, then WRITE_SIZE;
+           both in KiB per dispatch) of ``bench.py --copy-mb N``: the HBM
+           bytes per dispatch of one kernel, each counter scaled by what it
+           reads for the plain N MiB device copy in the same run (which moves
+           exactly N MiB each way).  The summary records a hash of the
+           kernel's source files; bench.py reports the traffic only while
+           that hash still matches.
+
+Usage:
+  python -m mla_latent_cache_decode_amd.rocprof_summary stats --csv DIR/run_kernel_stats.csv \\
+      --command "..." --out profiles/x.txt
+  python -m mla_latent_cache_decode_amd.rocprof_summary traffic --fetch F.csv --write W.csv \\
+      --kernel mla_decode_kernel --copy-mb 1024 --command-fetch "..." --command-write "..." --out profiles/y.txt
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("csrc/decode.hip", "csrc/mla_internal.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(path: str) -> dict | None:
+    """Parse a traffic summary written by this module; None if absent/unparsable."""
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    try:
+        return {"source_hash": vals["source_hash"], "bytes_per_launch": int(vals["hbm_bytes_per_launch"]),
+                "read_bytes": int(vals["read_bytes_per_launch"]),
+                "write_bytes": int(vals["write_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def _stats(args) -> str:
+    rows = list(csv.DictReader(open(args.csv)))
+    lines = [f"command: {args.command}", "", f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'min_us':>10} "
+             f"{'max_us':>10} {'pct':>6}"]
+    for r in rows:
+        name = r["Name"]
+        short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0][:60]
+        lines.append(f"{short:<60} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                     f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+                     f"{float(r['Percentage']):>6.2f}")
+    return "\n".join(lines) + "\n"
+
+
+def _per_kernel(path: str, counter: str) -> dict:
+    out: dict[str, list[tuple[int, float]]] = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return out
+
+
+def _traffic(args) -> str:
+    copy_bytes = args.copy_mb * (1 << 20)
+    res = {}
+    for tag, path, counter in (("read", args.fetch, "FETCH_SIZE"), ("write", args.write, "WRITE_SIZE")):
+        pk = _per_kernel(path, counter)
+        copies = [v for k, vs in pk.items() if "copyBuffer" in k for v in vs]
+        if not copies:
+            sys.exit(f"no copy kernel in {path}")
+        _, copy_kib = max(copies)                       # the big calibration copy
+        factor = copy_bytes / (copy_kib * 1024.0)
+        mine = [v for k, vs in pk.items() if args.kernel in k for _, v in vs]
+        if not mine:
+            sys.exit(f"no {args.kernel} dispatch in {path}")
+        kib = statistics.mean(mine)
+        res[tag] = (kib, factor, len(mine), copy_kib)
+    rb = int(round(res["read"][0] * 1024 * res["read"][1]))
+    wb = int(round(res["write"][0] * 1024 * res["write"][1]))
+    lines = [
+        f"kernel: {args.kernel}",
+        f"workload: {args.workload}",
+        f"source_hash: {kernel_source_hash()}",
+        f"read_bytes_per_launch: {rb}",
+        f"write_bytes_per_launch: {wb}",
+        f"hbm_bytes_per_launch: {rb + wb}",
+        "",
+        f"FETCH_SIZE: {res['read'][0]:.1f} KiB/dispatch over {res['read'][2]} dispatches; "
+        f"the {args.copy_mb} MiB copy read {res['read'][3]:.1f} KiB -> factor {res['read'][1]:.4f}",
+        f"WRITE_SIZE: {res['write'][0]:.1f} KiB/dispatch over {res['write'][2]} dispatches; "
+        f"the {args.copy_mb} MiB copy wrote {res['write'][3]:.1f} KiB -> factor {res['write'][1]:.4f}",
+        "",
+        f"command (fetch): {args.command_fetch}",
+        f"command (write): {args.command_write}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-mb", type=int, required=True)
+    t.add_argument("--command-fetch", required=True)
+    t.add_argument("--command-write", required=True)
+    t.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    text = _stats(args) if args.mode == "stats" else _traffic(args)
+    with open(args.out, "w") as f:
+        f.write(text)
+    print(text, end="")
+
+
+if __name__ == "__main__":
+    main()
