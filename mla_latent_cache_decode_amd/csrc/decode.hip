@@ -63,6 +63,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define CONST_AS __attribute__((address_space(4)))
@@ -72,22 +74,18 @@ constexpr int kTileBytes = kPage * kD * 2;      // 73728: one page of 16-bit ele
 constexpr int kKSteps = kD / 16;                // 36 MFMA k-steps for Q.K^T
 constexpr int kMdBlocks = kDc / 32;             // 16 output blocks of 32 dims
 constexpr int kPvSteps = 4 * kMdBlocks;         // 64 MFMA steps for P.V
-constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;   // 18 LDS-direct loads
-constexpr int kFp8StageBytes = kPage * kFp8RowBytes;   // 38912
-constexpr int kFp8Loads = kFp8StageBytes / 1024;       // 38
 constexpr float kRescaleTau = 15.0f;            // log2 units: p <= 2^15 stays inside fp16
 constexpr int kQkAhead = 2;                     // K fragment prefetch distance (k-steps)
 constexpr int kPvAhead = 2;                     // V fragment prefetch distance (steps)
 
-constexpr int kLdsTiles = 2 * kTileBytes;                       // 147456
-constexpr int kLdsTilesFp8 = kTileBytes + 2 * kFp8StageBytes;   // 151552
-constexpr int kScanInts = 16;                                   // planner scratch
+constexpr int kLdsTiles = 2 * kTileBytes;       // 147456: two fp16 tiles
+constexpr int kQRegSteps = kDc / 16;            // 32 k-steps (q_abs) whose Q fragments live in VGPRs
+constexpr int kQLdsSteps = kKSteps - kQRegSteps; // 4 k-steps (q_R) whose fragments live in LDS
+constexpr int kQLdsBytes = 4 * kQLdsSteps * 1024;  // 16384: 4 waves x 4 fragments x 64 lanes x 16 B
+constexpr int kLdsBytes = kLdsTiles + kQLdsBytes;  // 163840 = all of a CU's LDS
 
 static_assert(kChunks % 8 == 0, "row must be whole 64-dim column blocks");
-static_assert(kFp8StageBytes % 1024 == 0, "fp8 page must be whole 1 KiB load groups");
 
-// s_waitcnt immediate for "vmcnt <= n", other counters unconstrained (gfx9 encoding).
-#define VMCNT_IMM(n) ((((n) & 0xF)) | ((((n) >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8))
 #define LGKMCNT0_IMM 0xC07F
 
 template <int I, int N, typename F>
@@ -100,13 +98,20 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // Read-only per-call metadata (block table, lengths) is read through the
 // constant address space so the loads are scalar (SMEM): a vector load here
-// would have to wait on vmcnt, which also counts the in-flight page prefetch.
+// would have to wait on vmcnt, which also counts the in-flight page loads.
 template <typename T>
 __device__ __forceinline__ T ld_const(const T* p) {
     return *(const CONST_AS T*)p;
 }
 
-__device__ __forceinline__ int sw(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// Slot swizzle of token t: bits (t1, t2, t3) of t become slot bits (2, 1, 0).
+// LDS serves 16 lanes of a 128-bit access per pass over 64 banks.  A row
+// read of 16 consecutive tokens (Q.K^T fragments, fp8 stores) then hits 16
+// distinct 16-byte slots: even tokens cover slots 0..7 of the 256-byte bank
+// window, odd tokens 8..15, each through a bijection of (t1, t2, t3).  The
+// transposed PV reads touch tokens T, T+1, T+2, T+3 (T = 0 mod 4) in four
+// adjacent chunks; slot bit 2 = t1 separates T from T+2 (and T+1 from T+3).
+__device__ __forceinline__ int sw(int t) { return (((t >> 1) & 1) << 2) | (((t >> 2) & 1) << 1) | ((t >> 3) & 1); }
 
 // byte offset of (token t, chunk c) inside a tile (16-bit elements)
 __device__ __forceinline__ int tile_off(int t, int c) {
@@ -129,7 +134,7 @@ __device__ __forceinline__ float pair_sum(float v) {
 }
 
 // Workgroup barrier without a memory fence: a fence would make the compiler
-// wait for the in-flight LDS-direct prefetch of the next page as well.
+// wait for every in-flight page load as well.
 // Callers wait for exactly what they need (s_waitcnt) before it; the empty
 // asm statements stop the compiler from moving memory accesses across it.
 __device__ __forceinline__ void wg_barrier() {
@@ -159,9 +164,17 @@ __device__ __forceinline__ float scale_acc(float x, float alpha) {
 // being hoisted out of the page loop, where they would occupy registers for
 // the whole kernel and push the register allocator into spilling.
 __device__ __forceinline__ int opaque_lane() {
-    int l = __lane_id();
-    asm volatile("" : "+v"(l));
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
     return l;
+}
+
+// A copy of a lane value that the compiler must materialise where it is
+// used: offsets derived from it are then computed next to their load instead
+// of being hoisted out of the page loop (18 live offsets would spill).
+__device__ __forceinline__ int pinned(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -291,12 +304,22 @@ __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_i
 }
 
 // ---------------------------------------------------------------------------
-// page loaders (global -> LDS directly, 16 bytes per lane)
+// page pieces: HBM -> VGPRs -> (convert / dequantise) -> fp16 LDS tile
 // ---------------------------------------------------------------------------
+//
+// A page is moved by the four waves in pieces of one 16-byte vector load
+// per lane (1 KiB of bf16 per wave, or 16 fp8 codes plus their scale byte
+// per lane).  A piece is issued into registers well ahead of its use and
+// stored into the tile that the next tile step reads; both halves of the
+// work are spread over the MFMA steps of the current tile, so the memory
+// path, the conversion and the matrix cores overlap.
+//
+// Every piece load goes through one buffer descriptor per page whose size
+// is n_valid rows: lanes whose row lies past the visible tokens read zeros
+// (the rows are never fetched) and the tile receives finite zeros.  The
+// whole offset of a lane is in the VGPR offset, so the range check sees it.
 
-// Buffer descriptor over [base, base + bytes): lanes whose offset falls past
-// `bytes` read zeros, which is how rows beyond the visible tokens are kept
-// out of the tile (they are never fetched, and the LDS gets finite zeros).
+// Buffer descriptor over [base, base + bytes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int bytes) {
     // both inputs are wave-uniform; say so, or the compiler wraps each load
     // in a waterfall loop
@@ -308,135 +331,118 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base,
                                              0x00020000);
 }
 
-// bf16 page into the swizzled tile.  Load instruction n (0..71) fills tile
-// slots [64n, 64n + 64); lane i of it carries token ((n & 7) << 3) + (i >> 3)
-// of column block n >> 3.  The lane part of the source offset is the
-// constant lane_off (< 8 rows), the rest is a uniform offset.  A full page
-// uses one descriptor; a partial page (the last of a sequence) gives every
-// load its own descriptor whose size admits only rows below n_valid.  Wave w
-// issues instructions 18w .. 18w+17, one per load(i) call, so the caller can
-// spread them over other work.
-struct Bf16PageLoader {
-    const uint8_t* page;
-    LDS_AS uint8_t* tile;
-    int wave, lane_off, n_valid;
-    __amdgpu_buffer_rsrc_t full;
+// bf16 rows.  Wave w moves pieces n = 18w + k, k < 18.  Piece n covers the
+// 64-dim column block n >> 3 of tokens 8(n & 7) .. 8(n & 7) + 7: lane i
+// carries token 8(n & 7) + (i >> 3), chunk 8(n >> 3) + (i & 7).  In the tile
+// the piece is the contiguous 1 KiB at n * 1024 (see tile_off).
+struct Bf16Pieces {
+    static constexpr int kPieces = 18;
+    // a page moves in four batches (pieces [0,5), [5,9), [9,14), [14,18)),
+    // each stored and followed by the next one's loads at a step below
+    static constexpr int kBatches = 4;
+    static constexpr int kStage = 5;            // staging slots (largest batch)
+    __device__ static constexpr int first(int b) { return b == 0 ? 0 : b == 1 ? 5 : b == 2 ? 9 : b == 3 ? 14 : 18; }
+    // slot k of hook h runs at step kQkHooks[h] + k * kQkStride (Q.K^T, batches
+    // 0 and 1) or kPvHooks[h - 2] + k * kPvStride (P.V, batches 2 and 3):
+    // LDS stores are costly, so they are spread out
+    static constexpr int kQkHooks[2] = {2, 19};
+    static constexpr int kQkStride = 3;
+    static constexpr int kPvHooks[2] = {2, 34};
+    static constexpr int kPvStride = 6;
+    typedef u32x4 Stage;
 
-    __device__ __forceinline__ Bf16PageLoader(const uint8_t* page_, LDS_AS uint8_t* tile_, int wave_,
-                                              int lane_off_, int n_valid_)
-        : page(page_), tile(tile_), wave(wave_), lane_off(lane_off_), n_valid(n_valid_) {
-        full = make_rsrc(page, kPage * kBf16RowBytes);
+    int src_lane;       // (i >> 3) * 1152 + (i & 7) * 16
+    int dst_lane;       // tile_off(i >> 3, i & 7)
+
+    __device__ __forceinline__ explicit Bf16Pieces(int lane) {
+        src_lane = (lane >> 3) * kBf16RowBytes + ((lane & 7) << 4);
+        dst_lane = tile_off(lane >> 3, lane & 7);
     }
-    __device__ __forceinline__ void load(int i) const {
-        const int n = wave * kLoadsPerWave + i;
-        const int row_blk = (n & 7) << 3;
-        if (n_valid >= kPage) {
-            const int soff = row_blk * kBf16RowBytes + ((n >> 3) << 7);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(full, (LDS_AS void*)(tile + n * 1024), 16, lane_off, soff, 0,
-                                                     0);
-        } else {
-            const int rows = min(max(n_valid - row_blk, 0), 8);
-            const __amdgpu_buffer_rsrc_t r =
-                make_rsrc(page + row_blk * kBf16RowBytes + ((n >> 3) << 7), rows * kBf16RowBytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(tile + n * 1024), 16, lane_off, 0, 0, 0);
+    __device__ __forceinline__ static int piece(int wave, int k) { return wave * kPieces + k; }
+
+    __device__ __forceinline__ void issue(Stage& s, __amdgpu_buffer_rsrc_t r, int wave, int k) const {
+        const int n = piece(wave, k);
+        const int off = (n & 7) * 8 * kBf16RowBytes + ((n >> 3) << 7);
+        s = __builtin_amdgcn_raw_buffer_load_b128(r, pinned(src_lane) + off, 0, 0);
+    }
+    __device__ __forceinline__ void store(const Stage& s, LDS_AS uint8_t* tile, int wave, int k) const {
+        u32x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // bf16 -> fp32 is a shift; fp32 -> fp16 rounds to nearest even,
+            // exact for values inside the fp16 range
+            const float lo = __builtin_bit_cast(float, s[e] << 16);
+            const float hi = __builtin_bit_cast(float, s[e] & 0xFFFF0000u);
+            h[e] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
         }
+        // the piece's tokens are 8(n & 7) + (i >> 3); for odd n bit 3 of the
+        // token is set, which flips the low slot bit of the swizzle
+        const int n = piece(wave, k);
+        *(LDS_AS u32x4*)(tile + n * 1024 + (dst_lane ^ ((n & 1) << 4))) = h;
     }
 };
 
-// fp8 page, row-major into a staging buffer; waves 0,1 issue 10 loads, 2,3 issue 9.
-__device__ __forceinline__ void load_page_fp8(const uint8_t* page, LDS_AS uint8_t* stage, int wave,
-                                              int lane, int n_valid) {
-    const int valid_bytes = n_valid * kFp8RowBytes;
-#pragma unroll
-    for (int i = 0; i < 10; ++i) {
-        const int n = wave + 4 * i;
-        if (n < kFp8Loads) {
-            const int bytes = min(max(valid_bytes - n * 1024, 0), 1024);
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(page + n * 1024, bytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(stage + n * 1024), 16, lane * 16, 0, 0,
-                                                     0);
-        }
+// fp8 rows (D e4m3 codes, D/32 e8m0 scales, 16-byte stride).  Wave w moves
+// tokens 16w .. 16w + 15 in pieces k < 9: lane i carries token 16w + (i & 15),
+// codes 16j .. 16j + 15 with j = 4k + (i >> 4), and their scale byte j / 2.
+// The 16 dequantised halves are tile chunks 2j and 2j + 1 of that token.
+struct Fp8Pieces {
+    static constexpr int kPieces = 9;
+    // three batches of three pieces
+    static constexpr int kBatches = 3;
+    static constexpr int kStage = 3;
+    __device__ static constexpr int first(int b) { return 3 * b; }
+    static constexpr int kQkHooks[2] = {3, 20};
+    static constexpr int kQkStride = 5;
+    static constexpr int kPvHooks[1] = {4};
+    static constexpr int kPvStride = 8;
+    struct Stage {
+        u32x4 codes;
+        uint32_t scale;
+    };
+
+    int src_lane;       // token * 608 + 16 * (i >> 4)
+    int dst_lane;       // tile_off(token, 2 * (i >> 4)) without the column block
+
+    __device__ __forceinline__ Fp8Pieces(int lane, int wave) {
+        const int t = wave * 16 + (lane & 15);
+        src_lane = t * kFp8RowBytes + ((lane >> 4) << 4);
+        dst_lane = tile_off(t, 2 * (lane >> 4));
     }
-}
-
-__device__ __forceinline__ float e8m0_to_float(uint32_t e) {
-    // 2^(e-127); e = 0 is the fp32 subnormal 2^-127, e = 255 is NaN
-    uint32_t bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : (e << 23));
-    return __builtin_bit_cast(float, bits);
-}
-
-// Dequantise a staged fp8 page into the fp16 tile (all 256 threads, 18
-// units of 8 values each, in two batches of 9: a batch's reads are all
-// issued before its first conversion so the LDS round trips overlap).
-__device__ __forceinline__ void convert_fp8_page(const LDS_AS uint8_t* stage, LDS_AS uint8_t* tile,
-                                                 int tid) {
-    constexpr int kUnits = kPage * kChunks / kDecodeThreads;
-    constexpr int kBatch = kUnits / 2;
-    static_for<0, 2>([&](auto h_c) {
-        constexpr int h = decltype(h_c)::value;
-        u32x2 codes[kBatch];
-        uint32_t sc[kBatch];
-        static_for<0, kBatch>([&](auto k_c) {
-            constexpr int k = decltype(k_c)::value;
-            const int u = tid + kDecodeThreads * (h * kBatch + k);
-            const int t = u / kChunks;
-            const int c = u - t * kChunks;
-            const LDS_AS uint8_t* row = stage + t * kFp8RowBytes;
-            codes[k] = *(const LDS_AS u32x2*)(row + c * 8);
-            sc[k] = row[kD + (c >> 2)];
-        });
-        static_for<0, kBatch>([&](auto k_c) {
-            constexpr int k = decltype(k_c)::value;
-            const int u = tid + kDecodeThreads * (h * kBatch + k);
-            const int t = u / kChunks;
-            const int c = u - t * kChunks;
-            const float scale = e8m0_to_float(sc[k]);
-            f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[k][0], scale, false);
-            f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[k][0], scale, true);
-            f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[k][1], scale, false);
-            f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[k][1], scale, true);
-            f16x8 v = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-            *(LDS_AS f16x8*)(tile + tile_off(t, c)) = v;
-        });
-    });
-}
-
-// Convert a landed bf16 tile to fp16 in place (all 256 threads, 18 chunks
-// of 16 bytes each, read and written by the same thread), in two batches
-// of 9 whose reads are all issued before the first conversion.  If a loader
-// is given, its 18 page loads (into the other buffer) are interleaved with
-// the conversions, so the load path works in the background.
-struct NoLoads {
-    __device__ __forceinline__ void load(int) const {}
-};
-
-template <typename Loader>
-__device__ __forceinline__ void convert_bf16_tile(LDS_AS uint8_t* tile, int tid, Loader ld) {
-    constexpr int kUnits = kTileBytes / 16 / kDecodeThreads;
-    constexpr int kBatch = kUnits / 2;
-    LDS_AS uint8_t* base = tile + tid * 16;
-    static_for<0, 2>([&](auto h_c) {
-        constexpr int h = decltype(h_c)::value;
-        u32x4 v[kBatch];
-        static_for<0, kBatch>([&](auto k_c) {
-            constexpr int k = decltype(k_c)::value;
-            v[k] = *(const LDS_AS u32x4*)(base + (h * kBatch + k) * kDecodeThreads * 16);
-        });
-        static_for<0, kBatch>([&](auto k_c) {
-            constexpr int k = decltype(k_c)::value;
-            ld.load(h * kBatch + k);
-            u32x4 r;
+    __device__ __forceinline__ void issue(Stage& s, __amdgpu_buffer_rsrc_t r, int, int k) const {
+        s.codes = __builtin_amdgcn_raw_buffer_load_b128(r, pinned(src_lane) + k * 64, 0, 0);
+        // the scale byte of codes 16j.. sits at token * 608 + 576 + j / 2;
+        // derived here rather than held, to spare a register
+        const int l = opaque_lane();
+        const int scl = pinned(src_lane) - ((l >> 4) << 4) + kD + (l >> 5);
+        s.scale = __builtin_amdgcn_raw_buffer_load_b8(r, scl + k * 2, 0, 0);
+    }
+    __device__ __forceinline__ void store(const Stage& s, LDS_AS uint8_t* tile, int, int k) const {
+        // 2^(e-127) as fp32 bits e << 23.  e = 255 (NaN) also sets the top
+        // mantissa bit, making a quiet NaN instead of infinity.  e = 0 gives
+        // 0 rather than 2^-127: every e4m3 value times 2^-127 rounds to a
+        // signed zero in fp16 anyway, so the dequantised halves are the same.
+        const uint32_t e = s.scale & 0xFF;
+        const uint32_t bits = (((e + 1) >> 8) << 22) | (e << 23);
+        const float scale = __builtin_bit_cast(float, bits);
+        // chunks 2j and 2j + 1 sit in adjacent 16-byte slots (the swizzle
+        // flips at most the low slot bit between them); one at a time keeps
+        // the temporaries to four registers
+        LDS_AS uint8_t* d = tile + k * 8192;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = __builtin_bit_cast(float, v[k][i] << 16);
-                const float hi = __builtin_bit_cast(float, v[k][i] & 0xFFFF0000u);
-                const f16x2 hv = {(_Float16)lo, (_Float16)hi};
-                r[i] = __builtin_bit_cast(uint32_t, hv);
+        for (int c = 0; c < 2; ++c) {
+            u32x4 h;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                h[2 * q + 0] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.codes[2 * c + q], scale, false));
+                h[2 * q + 1] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.codes[2 * c + q], scale, true));
             }
-            *(LDS_AS u32x4*)(base + (h * kBatch + k) * kDecodeThreads * 16) = r;
-        });
-    });
-}
+            *(LDS_AS u32x4*)(d + (dst_lane ^ (c << 4))) = h;
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------
 // per-tile compute of one wave: 32 heads x 64 tokens
@@ -448,8 +454,13 @@ struct WaveState {
     bool o_zero;             // nothing accumulated yet (wave-uniform)
 };
 
-__device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f16x8 (&qf)[kKSteps],
-                                             WaveState& st, int n_valid, float scale_log2) {
+// One tile step of one wave.  qk_hook(ks) runs inside Q.K^T step ks and
+// pv_hook(step) inside P.V step `step` (both compile-time); they carry the
+// page pipeline's loads and LDS stores so that these issue between MFMAs.
+template <typename QkHook, typename PvHook>
+__device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f16x8 (&qf)[kQRegSteps],
+                                             const LDS_AS uint8_t* qr, WaveState& st, int n_valid,
+                                             float scale_log2, QkHook&& qk_hook, PvHook&& pv_hook) {
     const int lane = opaque_lane();
     const int hi = lane >> 5;
 
@@ -460,20 +471,25 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
 #pragma unroll
     for (int k = 0; k < 4; ++k) k_off[k] = tile_off(lane & 31, 2 * k + hi);
     f32x16 s0 = {}, s1 = {};
-    f16x8 kf[kQkAhead + 1][2];
-    auto read_k = [&](auto ks_c, f16x8 (&dst)[2]) {
+    f16x8 kf[kQkAhead + 1][3];      // [2]: the q_R fragment of the last k-steps
+    auto read_k = [&](auto ks_c, f16x8 (&dst)[3]) {
         constexpr int ks = decltype(ks_c)::value;
         const LDS_AS uint8_t* base = tile + k_off[ks & 3] + (ks >> 2) * 8192;
         dst[0] = *(const LDS_AS f16x8*)(base);
         dst[1] = *(const LDS_AS f16x8*)(base + 4096);
+        if constexpr (ks >= kQRegSteps) dst[2] = *(const LDS_AS f16x8*)(qr + (ks - kQRegSteps) * 1024);
     };
     static_for<0, kQkAhead>([&](auto i) { read_k(i, kf[decltype(i)::value]); });
     static_for<0, kKSteps>([&](auto ks_c) {
         constexpr int ks = decltype(ks_c)::value;
         if constexpr (ks + kQkAhead < kKSteps)
             read_k(std::integral_constant<int, ks + kQkAhead>{}, kf[(ks + kQkAhead) % (kQkAhead + 1)]);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks % (kQkAhead + 1)][0], qf[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks % (kQkAhead + 1)][1], qf[ks], s1, 0, 0, 0);
+        qk_hook(ks_c);
+        f16x8 qb;
+        if constexpr (ks < kQRegSteps) qb = qf[ks];
+        else qb = kf[ks % (kQkAhead + 1)][2];
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks % (kQkAhead + 1)][0], qb, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks % (kQkAhead + 1)][1], qb, s1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     });
     // the scores feed VALU work (softmax): keep them in arch VGPRs
@@ -529,20 +545,22 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
 
     // ---- O^T += V^T P^T.  Step s covers (kb = s >> 4, md = s & 15); its V^T
     // fragment is two transposed reads (tokens kb*16 + e4*8 + tok_lane, dims
-    // md*32 + dim_lane).  The reads are issued as asm because the compiler
-    // cannot tell they do not alias the page prefetch still in flight and
-    // would wait for it (vmcnt(0)); the lgkmcnt wait is tied to the
-    // fragment so the MFMA cannot move above it, and fragment buffers rotate
-    // so a read never overwrites an operand of the MFMA issued just before.
+    // md*32 + dim_lane), issued kPvAhead steps ahead into rotating buffers.
     __builtin_amdgcn_sched_barrier(0);
-    uint32_t vp[2];
+    // vp[m][e]: tokens 8e + tok (the swizzle sees bit 3 of the token, which
+    // flips the low slot bit: address ^ 16), dims m*32 + dim; the step's
+    // column block and 16-token block are added as immediate offsets
+    const LDS_AS uint8_t* vp[2][2];
     {
         const int g = lane >> 4, li = lane & 15;
         const int tok = ((g >> 1) << 2) + (li >> 2);
         const int dim = ((g & 1) << 4) + ((li & 3) << 2);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-            vp[m] = (uint32_t)(uintptr_t)(tile + tile_off(tok, (m * 32 + dim) >> 3) + (dim & 7) * 2);
+        for (int m = 0; m < 2; ++m) {
+            const int o = tile_off(tok, (m * 32 + dim) >> 3) + (dim & 7) * 2;
+            vp[m][0] = tile + o;
+            vp[m][1] = tile + (o ^ 16) + 8 * 128;
+        }
     }
     constexpr int kVBufs = kPvAhead + 2;
     f16x8 vf[kVBufs];
@@ -550,27 +568,19 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
         constexpr int step = decltype(step_c)::value;
         constexpr int kb_ = step >> 4, md = step & 15;
         constexpr int off = (md >> 1) * 8192 + kb_ * 16 * 128;
-        f16x4 v0, v1;
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v0) : "v"(vp[md & 1]), "i"(off));
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v1) : "v"(vp[md & 1]), "i"(off + 8 * 128));
-        return f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][0] + off));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][1] + off));
+        return __builtin_bit_cast(f16x8, i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
     };
-    static_assert(kPvAhead == 2, "the lgkmcnt immediates below assume two steps in flight");
     static_for<0, kPvAhead>([&](auto i) { vf[decltype(i)::value] = read_v(i); });
     static_for<0, kPvSteps>([&](auto step_c) {
         constexpr int step = decltype(step_c)::value;
-        constexpr int ahead = (step + kPvAhead < kPvSteps) ? kPvAhead : (kPvSteps - 1 - step);
-        if constexpr (step + kPvAhead < kPvSteps) {
+        if constexpr (step + kPvAhead < kPvSteps)
             vf[(step + kPvAhead) % kVBufs] = read_v(std::integral_constant<int, step + kPvAhead>{});
-            // the previous MFMA's operand stays allocated across this read
-            if constexpr (step > 0) asm volatile("" ::"v"(vf[(step - 1) % kVBufs]));
-        }
-        if constexpr (ahead == 2) asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(vf[step % kVBufs]));
-        else if constexpr (ahead == 1) asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(vf[step % kVBufs]));
-        else asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(vf[step % kVBufs]));
+        pv_hook(step_c);
         st.o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[step % kVBufs], pf[step >> 4], st.o[step & 15],
                                                                   0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);     // keep [read s+ahead, wait, mfma s] in order
+        __builtin_amdgcn_sched_barrier(0);
     });
     // keep the accumulator's home in AGPRs (it is only touched by MFMA in the
     // steady state); VALU users copy out and back
@@ -583,11 +593,39 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
 // the decode kernel
 // ---------------------------------------------------------------------------
 template <bool kFp8>
+struct PiecesOf;
+template <>
+struct PiecesOf<false> {
+    typedef Bf16Pieces type;
+    static constexpr int kRowBytes = kBf16RowBytes;
+    __device__ __forceinline__ static Bf16Pieces make(int lane, int) { return Bf16Pieces(lane); }
+};
+template <>
+struct PiecesOf<true> {
+    typedef Fp8Pieces type;
+    static constexpr int kRowBytes = kFp8RowBytes;
+    __device__ __forceinline__ static Fp8Pieces make(int lane, int wave) { return Fp8Pieces(lane, wave); }
+};
+
+template <bool kFp8>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArgs a) {
-    constexpr int kTileRegion = kFp8 ? kLdsTilesFp8 : kLdsTiles;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kTileRegion + kScanInts * 4];
+    typedef typename PiecesOf<kFp8>::type Pieces;
+    typedef typename Pieces::Stage Stage;
+    constexpr int kPieces = Pieces::kPieces;
+    constexpr int kNB = Pieces::kBatches;
+    constexpr int kS = Pieces::kStage;
+    constexpr int kRowBytes = PiecesOf<kFp8>::kRowBytes;
+    // batch b is stored by hook b: the first two hooks sit in Q.K^T, the rest in P.V
+    constexpr int kNPv = kNB - 2;
+    static_assert(Pieces::first(kNB) == kPieces, "batches cover the page");
+    constexpr int kQs = Pieces::kQkStride, kPs = Pieces::kPvStride;
+    static_assert(Pieces::kQkHooks[0] + (kS - 1) * kQs < Pieces::kQkHooks[1] &&
+                      Pieces::kQkHooks[1] + (kS - 1) * kQs < kKSteps, "Q.K^T hooks must fit");
+    static_assert(Pieces::kPvHooks[kNPv - 1] + (kS - 1) * kPs < kPvSteps, "P.V hooks must fit");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
-    int* sbuf = (int*)(smem + kTileRegion);
+    int* sbuf = (int*)smem;                 // planner scratch; dead before the first tile store
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -605,22 +643,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
     const int64_t Q = start.quota;
     const int64_t w_lo = (int64_t)worker * Q, w_hi = w_lo + Q;
 
-    // zero the LDS once so that nothing in it is ever uninitialised
-    {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        for (int off = tid * 16; off < kTileRegion; off += kDecodeThreads * 16) *(LDS_AS f32x4*)(lds + off) = z;
-    }
-    __syncthreads();
-
-    LDS_AS uint8_t* tile_c = lds;                          // fp8: the single fp16 tile
-    LDS_AS uint8_t* bufs[2];
-    if (kFp8) {
-        bufs[0] = lds + kTileBytes;
-        bufs[1] = lds + kTileBytes + kFp8StageBytes;
-    } else {
-        bufs[0] = lds;
-        bufs[1] = lds + kTileBytes;
-    }
+    LDS_AS uint8_t* const tiles[2] = {lds, lds + kTileBytes};
+    // this wave's q_R fragments, lane-major: fragment f of lane l at f*1024 + l*16
+    LDS_AS uint8_t* const qr_lds = lds + kLdsTiles + wave * (kQLdsSteps * 1024) + (tid & 63) * 16;
 
     int64_t cost = start.cost;
     int slot_base = start.slot;
@@ -642,35 +667,25 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
 
         const int n_vis = L - a.s_q + 1 + j_wave;           // tokens this wave may see
         const int n_load = L - a.s_q + 1 + j_last;          // tokens the workgroup loads
-        const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks;
 
-        // issue(p, phys, dst): load logical page p (physical page phys).  The
-        // block-table entry is read a tile ahead of its use (next_phys), so
-        // the scalar load's latency is not on the issue path.
-        auto bf16_loader = [&](int p, int phys, LDS_AS uint8_t* dst) {
-            const int ol = opaque_lane();
-            const int ld_tok = ol >> 3;                           // bf16 loader lane offset
-            return Bf16PageLoader(a.kv + (int64_t)phys * a.page_bytes, dst, wave,
-                                  ld_tok * kBf16RowBytes + (((ol & 7) ^ sw(ld_tok)) << 4),
-                                  min(max(n_load - p * kPage, 0), kPage));
+        // Block-table entries are read with vector loads (ordered with the
+        // page loads on vmcnt; a scalar load would share lgkmcnt with the
+        // LDS traffic and make every LDS wait a full drain).  Entries of
+        // pages at or past p_hi read 0 and are not used.
+        const __amdgpu_buffer_rsrc_t bt =
+            make_rsrc((const uint8_t*)(a.block_table + (int64_t)b * a.max_blocks), p_hi * 4);
+        auto load_phys = [&](int p) -> int { return __builtin_amdgcn_raw_buffer_load_b32(bt, p * 4, 0, 0); };
+        // descriptor of logical page p (physical page phys); size 0 past p_hi
+        auto page_rsrc = [&](int p, int phys) {
+            const int nv = p < p_hi ? min(max(n_load - p * kPage, 0), kPage) : 0;
+            return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes, nv * kRowBytes);
         };
-        auto issue = [&](int p, int phys, LDS_AS uint8_t* dst) {
-            if (kFp8) {
-                load_page_fp8(a.kv + (int64_t)phys * a.page_bytes, dst, wave, opaque_lane(),
-                              min(max(n_load - p * kPage, 0), kPage));
-            } else {
-                const Bf16PageLoader ld = bf16_loader(p, phys, dst);
-#pragma unroll
-                for (int i = 0; i < kLoadsPerWave; ++i) ld.load(i);
-            }
-        };
-        auto phys_of = [&](int p) -> int { return p < p_hi ? ld_const(bt + p) : 0; };
 
         // this wave's 32 query rows as MFMA B operands (q_abs || q_R): bf16
         // loaded, scaled per head by 2^-sh so the head's max |q| lands in
         // [2^14, 2^15), converted to fp16 (exact up to fp16 subnormals); the
         // head's softmax scale absorbs 2^sh
-        f16x8 qf[kKSteps];
+        f16x8 qf[kKSteps];      // the q_R part moves to LDS after the conversion
         float scale_lane;
         WaveState st;
         st.m = -__builtin_inff();
@@ -678,17 +693,33 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         st.o_zero = true;
 #pragma unroll
         for (int md = 0; md < kMdBlocks; ++md) st.o[md] = f32x16{};
+        const int lane0 = tid & 63;
         {
-            const int lane = tid & 63;
-            const int row = active ? row0 + (lane & 31) : 0;
-            const uint16_t* qrow = a.q + ((int64_t)b * M + row) * kD + (lane >> 5) * 8;
+            const int row = active ? row0 + (lane0 & 31) : 0;
+            const uint16_t* qrow = a.q + ((int64_t)b * M + row) * kD + (lane0 >> 5) * 8;
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = __builtin_bit_cast(f16x8, *(const bf16x8*)(qrow + ks * 16));
+        }
+
+        // first page of the segment, both batches, while the queries land
+        const Pieces pc = PiecesOf<kFp8>::make(opaque_lane(), wave);
+        const int phys0 = load_phys(p_lo);
+        const int phys1 = load_phys(p_lo + 1);
+        const __amdgpu_buffer_rsrc_t r0 = page_rsrc(p_lo, phys0);
+        Stage stg[kS], s0p[kPieces];
+        static_for<0, kPieces>([&](auto k) { pc.issue(s0p[k], r0, wave, k); });
+        __amdgpu_buffer_rsrc_t r_next = page_rsrc(p_lo + 1, phys1);
+        // block-table entries are loaded a tile before their use, so that
+        // reading them never waits on the loads issued after them
+        int phys2 = load_phys(p_lo + 2);
+
+        {
             float qmax = 0.f;
 #pragma unroll
             for (int ks = 0; ks < kKSteps; ++ks) {
-                const bf16x8 qb = *(const bf16x8*)(qrow + ks * 16);
+                const bf16x8 qb = __builtin_bit_cast(bf16x8, qf[ks]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf((float)qb[e]));
-                qf[ks] = __builtin_bit_cast(f16x8, qb);          // raw bits for now
             }
             qmax = pair_max(qmax);
             // exponent of qmax (a normal or zero float after the bf16 widening)
@@ -703,70 +734,78 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
                 for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)((float)qb[e] * down);
             }
             scale_lane = a.scale_log2 * up;
+            // the previous segment's last tile has retired its q_R reads (barrier)
+#pragma unroll
+            for (int ks = kQRegSteps; ks < kKSteps; ++ks)
+                *(LDS_AS f16x8*)(qr_lds + (ks - kQRegSteps) * 1024) = qf[ks];
         }
+        const f16x8(&qreg)[kQRegSteps] = *reinterpret_cast<const f16x8(*)[kQRegSteps]>(&qf[0]);
 
-        // Page pipeline.  bf16: two LDS tiles, a landed page is converted in
-        // place.  fp8: two staging buffers and one fp16 tile.  Per tile two
-        // workgroup barriers: "page p+1 landed and everyone is done with the
-        // tile" and "page p+1 converted".
-        auto wait_loads = [&](bool keep_one_page) {
-            // every load instruction is issued (rows past the end read zeros),
-            // so the counts are exact; the query loads are older than any page
-            if (keep_one_page) {
-                if (kFp8) {
-                    if (wave < 2) __builtin_amdgcn_s_waitcnt(VMCNT_IMM(10));
-                    else __builtin_amdgcn_s_waitcnt(VMCNT_IMM(9));
-                } else {
-                    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(kLoadsPerWave));
-                }
-            } else {
-                __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
-            }
-        };
-        // convert page p; bf16 may carry the loads of the page after next
-        auto convert = [&](int p, auto ld) {
-            if (kFp8) convert_fp8_page(bufs[(p - p_lo) & 1], tile_c, wave * 64 + opaque_lane());
-            else convert_bf16_tile(bufs[(p - p_lo) & 1], wave * 64 + opaque_lane(), ld);
-            __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
-            wg_barrier();
-        };
-
-        // prefetch (after the query loads, so that waiting for a page also
-        // covers the query fragments)
-        issue(p_lo, phys_of(p_lo), bufs[0]);
-        if (p_lo + 1 < p_hi) issue(p_lo + 1, phys_of(p_lo + 1), bufs[1]);
-        const int ahead = kFp8 ? 3 : 2;          // the page a tile's end issues
-        int next_phys = phys_of(p_lo + ahead - 1);
-        wait_loads(p_lo + 1 < p_hi);
+        static_for<0, kPieces>([&](auto k) {
+            pc.store(s0p[k], tiles[0], wave, k);
+            if constexpr (k < Pieces::first(1)) pc.issue(stg[k], r_next, wave, k);   // batch 0 of page p_lo + 1
+        });
+        __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
         wg_barrier();
-        convert(p_lo, NoLoads{});
-        if (kFp8 && p_lo + 2 < p_hi) issue(p_lo + 2, next_phys, bufs[0]);
 
+        // Page pipeline, one barrier per tile.  During tile p (read from
+        // tiles[p & 1]) page p + 1 moves into the other tile in three or
+        // four batches through one set of staging registers: each hook
+        // stores a batch (the first one was issued during the previous
+        // tile) and issues the next; the last hook issues batch 0 of page
+        // p + 2.
         for (int p = p_lo; p < p_hi; ++p) {
-            next_phys = phys_of(p + ahead);
-            const LDS_AS uint8_t* tile = kFp8 ? tile_c : bufs[(p - p_lo) & 1];
+            const LDS_AS uint8_t* tile = tiles[(p - p_lo) & 1];
+            LDS_AS uint8_t* tnext = tiles[(p - p_lo + 1) & 1];
+            const int phys_next = load_phys(p + 3);
+            __amdgpu_buffer_rsrc_t r2;
+            // hook h, slot k: store piece k of batch h (page p + 1) and load
+            // piece k of the next batch into the freed slot; the last batch
+            // is followed by batch 0 of page p + 2
+            auto move_piece = [&](auto h_c, auto k_c) {
+                constexpr int h = decltype(h_c)::value, k = decltype(k_c)::value;
+                constexpr int n = Pieces::first(h) + k;
+                if constexpr (n < Pieces::first(h + 1)) pc.store(stg[k], tnext, wave, n);
+                if constexpr (h + 1 < kNB) {
+                    constexpr int n2 = Pieces::first(h + 1) + k;
+                    if constexpr (n2 < Pieces::first(h + 2)) pc.issue(stg[k], r_next, wave, n2);
+                } else {
+                    if constexpr (k < Pieces::first(1)) pc.issue(stg[k], r2, wave, k);
+                }
+            };
+            auto qk_hook = [&](auto ks_c) {
+                constexpr int ks = decltype(ks_c)::value;
+                static_for<0, 2>([&](auto h_c) {
+                    constexpr int h = decltype(h_c)::value, at = Pieces::kQkHooks[h];
+                    if constexpr (ks >= at && (ks - at) % kQs == 0 && (ks - at) / kQs < kS)
+                        move_piece(std::integral_constant<int, h>{}, std::integral_constant<int, (ks - at) / kQs>{});
+                });
+                if constexpr (ks == kKSteps - 1) {
+                    r2 = page_rsrc(p + 2, phys2);
+                }
+            };
+            auto pv_hook = [&](auto step_c) {
+                constexpr int step = decltype(step_c)::value;
+                static_for<0, kNPv>([&](auto h_c) {
+                    constexpr int h = decltype(h_c)::value, at = Pieces::kPvHooks[h];
+                    if constexpr (step >= at && (step - at) % kPs == 0 && (step - at) / kPs < kS)
+                        move_piece(std::integral_constant<int, h + 2>{},
+                                   std::integral_constant<int, (step - at) / kPs>{});
+                });
+
+            };
             // inactive waves (rows beyond M) compute on row 0's query and
             // discard the result: keeping the call unconditional keeps the
             // accumulators out of control-flow merges
-            compute_tile(tile, qf, st, min(max(n_vis - p * kPage, 0), kPage), scale_lane);
-
-            __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);           // this wave's LDS reads retired
-            if (p + 1 < p_hi) {
-                // fp8 keeps page p+2 in flight; bf16 has only page p+1 outstanding
-                wait_loads(kFp8 && p + 2 < p_hi);
-                wg_barrier();
-                if (kFp8) {
-                    convert(p + 1, NoLoads{});
-                    if (p + 3 < p_hi) issue(p + 3, next_phys, bufs[(p + 1 - p_lo) & 1]);
-                } else if (p + 2 < p_hi) {
-                    convert(p + 1, bf16_loader(p + 2, next_phys, bufs[(p - p_lo) & 1]));
-                } else {
-                    convert(p + 1, NoLoads{});
-                }
-            } else {
-                wg_barrier();       // buffers are reused by the next segment
-            }
+            compute_tile(tile, qreg, qr_lds, st, min(max(n_vis - p * kPage, 0), kPage), scale_lane, qk_hook,
+                         pv_hook);
+            r_next = r2;
+            phys2 = phys_next;
+            __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);           // tile stores and reads retired
+            wg_barrier();
         }
+        // the last tiles issued loads of pages past p_hi: zero-size
+        // descriptors, nothing is fetched, and their registers are dead
 
         // epilogue: normalise and write final output or the split's partial
         if (active) {
