@@ -77,6 +77,7 @@ constexpr int kPvSteps = 4 * kMdBlocks;         // 64 MFMA steps for P.V
 constexpr float kRescaleTau = 15.0f;            // log2 units: p <= 2^15 stays inside fp16
 constexpr int kQkAhead = 2;                     // K fragment prefetch distance (k-steps)
 constexpr int kPvAhead = 2;                     // V fragment prefetch distance (steps)
+constexpr int kPMakeAt = 6;                     // P.V step (within a 16-step block) that builds the next P fragment
 
 constexpr int kLdsTiles = 2 * kTileBytes;       // 147456: two fp16 tiles
 constexpr int kQRegSteps = kDc / 16;            // 32 k-steps (q_abs) whose Q fragments live in VGPRs
@@ -337,18 +338,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base,
 // the piece is the contiguous 1 KiB at n * 1024 (see tile_off).
 struct Bf16Pieces {
     static constexpr int kPieces = 18;
-    // a page moves in four batches (pieces [0,5), [5,9), [9,14), [14,18)),
-    // each stored and followed by the next one's loads at a step below
-    static constexpr int kBatches = 4;
-    static constexpr int kStage = 5;            // staging slots (largest batch)
-    __device__ static constexpr int first(int b) { return b == 0 ? 0 : b == 1 ? 5 : b == 2 ? 9 : b == 3 ? 14 : 18; }
-    // slot k of hook h runs at step kQkHooks[h] + k * kQkStride (Q.K^T, batches
-    // 0 and 1) or kPvHooks[h - 2] + k * kPvStride (P.V, batches 2 and 3):
-    // LDS stores are costly, so they are spread out
-    static constexpr int kQkHooks[2] = {2, 19};
-    static constexpr int kQkStride = 3;
-    static constexpr int kPvHooks[2] = {2, 34};
-    static constexpr int kPvStride = 6;
+    // a page moves in five batches (pieces [0,4), [4,8), [8,12), [12,15),
+    // [15,18)).  Hook h stores batch h: its slot k runs in phase
+    // kHookPv[h] (0 = Q.K^T, 1 = P.V) at step kHookAt[h] + k * kHookStride[h].
+    // The hooks are spaced evenly in time over a tile (a Q.K^T step takes
+    // about twice a P.V step), so every batch gets the same time to land.
+    static constexpr int kBatches = 5;
+    static constexpr int kStage = 4;            // staging slots (largest batch)
+    __device__ static constexpr int first(int b) { return b <= 3 ? 4 * b : b == 4 ? 15 : 18; }
+    static constexpr int kHookPv[5] = {0, 0, 0, 1, 1};
+    static constexpr int kHookAt[5] = {0, 14, 28, 4, 34};
+    static constexpr int kHookStride[5] = {3, 3, 2, 6, 6};
     typedef u32x4 Stage;
 
     int src_lane;       // (i >> 3) * 1152 + (i & 7) * 16
@@ -392,10 +392,9 @@ struct Fp8Pieces {
     static constexpr int kBatches = 3;
     static constexpr int kStage = 3;
     __device__ static constexpr int first(int b) { return 3 * b; }
-    static constexpr int kQkHooks[2] = {3, 20};
-    static constexpr int kQkStride = 5;
-    static constexpr int kPvHooks[1] = {4};
-    static constexpr int kPvStride = 8;
+    static constexpr int kHookPv[3] = {0, 0, 1};
+    static constexpr int kHookAt[3] = {2, 22, 12};
+    static constexpr int kHookStride[3] = {5, 5, 10};
     struct Stage {
         u32x4 codes;
         uint32_t scale;
@@ -484,27 +483,33 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
         constexpr int ks = decltype(ks_c)::value;
         if constexpr (ks + kQkAhead < kKSteps)
             read_k(std::integral_constant<int, ks + kQkAhead>{}, kf[(ks + kQkAhead) % (kQkAhead + 1)]);
-        qk_hook(ks_c);
         f16x8 qb;
         if constexpr (ks < kQRegSteps) qb = qf[ks];
         else qb = kf[ks % (kQkAhead + 1)][2];
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks % (kQkAhead + 1)][0], qb, s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks % (kQkAhead + 1)][1], qb, s1, 0, 0, 0);
+        // the hook's VALU and memory work issues while the two MFMAs run
+        qk_hook(ks_c);
         __builtin_amdgcn_sched_barrier(0);
     });
     // the scores feed VALU work (softmax): keep them in arch VGPRs
     asm volatile("" : "+v"(s0), "+v"(s1));
 
     // ---- softmax.  Tokens >= n_valid (tail of the sequence / causal limit)
-    // are masked branch-free: excluded from the max and given p = 0.  The
-    // token of register r is c_r + 4*hi (+32 for s1); compare c_r with nv_lane.
+    // are masked: excluded from the max and given p = 0.  The token of
+    // register r is c_r + 4*hi (+32 for s1); compare c_r with nv_lane.
     const int nv_lane = n_valid - (hi << 2);
     float mx = -__builtin_inff();
+    if (n_valid >= kPage) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int c_r = ((r >> 2) << 3) + (r & 3);
-        mx = fmaxf(mx, c_r < nv_lane ? s0[r] : -__builtin_inff());
-        mx = fmaxf(mx, c_r + 32 < nv_lane ? s1[r] : -__builtin_inff());
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int c_r = ((r >> 2) << 3) + (r & 3);
+            mx = fmaxf(mx, c_r < nv_lane ? s0[r] : -__builtin_inff());
+            mx = fmaxf(mx, c_r + 32 < nv_lane ? s1[r] : -__builtin_inff());
+        }
     }
     mx = pair_max(mx);
     const float mx2 = mx * scale_log2;
@@ -522,26 +527,27 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
         }
         st.m = m_new;
     }
+    // P fragment kb (tokens of S^T registers 8(kb&1) .. +7 of s0 / s1) in
+    // fp16; fragment 0 now, the others inside the P.V loop, where their
+    // exponentials issue between MFMAs
     const float neg_m = -st.m;
     float lsum = 0.f;
+    auto make_p = [&](auto kb_c) -> f16x8 {
+        constexpr int kb = decltype(kb_c)::value;
+        const f32x16& sv = kb < 2 ? s0 : s1;
+        f16x8 f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int c_r = ((r >> 2) << 3) + (r & 3);
-        const float p0 = c_r < nv_lane ? fast_exp2(fmaf(s0[r], scale_log2, neg_m)) : 0.f;
-        const float p1 = c_r + 32 < nv_lane ? fast_exp2(fmaf(s1[r], scale_log2, neg_m)) : 0.f;
-        s0[r] = p0;
-        s1[r] = p1;
-        lsum += p0 + p1;
-    }
-    st.l += lsum;
+        for (int e = 0; e < 8; ++e) {
+            const int r = (kb & 1) * 8 + e;
+            const int c_r = ((r >> 2) << 3) + (r & 3) + (kb >= 2 ? 32 : 0);
+            const float x = c_r < nv_lane ? fast_exp2(fmaf(sv[r], scale_log2, neg_m)) : 0.f;
+            lsum += x;
+            f[e] = (_Float16)x;
+        }
+        return f;
+    };
     f16x8 pf[4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        pf[0][e] = (_Float16)s0[e];
-        pf[1][e] = (_Float16)s0[8 + e];
-        pf[2][e] = (_Float16)s1[e];
-        pf[3][e] = (_Float16)s1[8 + e];
-    }
+    pf[0] = make_p(std::integral_constant<int, 0>{});
 
     // ---- O^T += V^T P^T.  Step s covers (kb = s >> 4, md = s & 15); its V^T
     // fragment is two transposed reads (tokens kb*16 + e4*8 + tok_lane, dims
@@ -577,15 +583,19 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
         constexpr int step = decltype(step_c)::value;
         if constexpr (step + kPvAhead < kPvSteps)
             vf[(step + kPvAhead) % kVBufs] = read_v(std::integral_constant<int, step + kPvAhead>{});
-        pv_hook(step_c);
         st.o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[step % kVBufs], pf[step >> 4], st.o[step & 15],
                                                                   0, 0, 0);
+        // VALU and memory work issues while the MFMA runs
+        if constexpr ((step & 15) == kPMakeAt && (step >> 4) < 3)
+            pf[(step >> 4) + 1] = make_p(std::integral_constant<int, (step >> 4) + 1>{});
+        pv_hook(step_c);
         __builtin_amdgcn_sched_barrier(0);
     });
     // keep the accumulator's home in AGPRs (it is only touched by MFMA in the
     // steady state); VALU users copy out and back
 #pragma unroll
     for (int md = 0; md < kMdBlocks; ++md) asm volatile("" : "+a"(st.o[md]));
+    st.l += lsum;
     st.o_zero = false;
 }
 
@@ -610,18 +620,8 @@ struct PiecesOf<true> {
 template <bool kFp8>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArgs a) {
     typedef typename PiecesOf<kFp8>::type Pieces;
-    typedef typename Pieces::Stage Stage;
     constexpr int kPieces = Pieces::kPieces;
-    constexpr int kNB = Pieces::kBatches;
-    constexpr int kS = Pieces::kStage;
     constexpr int kRowBytes = PiecesOf<kFp8>::kRowBytes;
-    // batch b is stored by hook b: the first two hooks sit in Q.K^T, the rest in P.V
-    constexpr int kNPv = kNB - 2;
-    static_assert(Pieces::first(kNB) == kPieces, "batches cover the page");
-    constexpr int kQs = Pieces::kQkStride, kPs = Pieces::kPvStride;
-    static_assert(Pieces::kQkHooks[0] + (kS - 1) * kQs < Pieces::kQkHooks[1] &&
-                      Pieces::kQkHooks[1] + (kS - 1) * kQs < kKSteps, "Q.K^T hooks must fit");
-    static_assert(Pieces::kPvHooks[kNPv - 1] + (kS - 1) * kPs < kPvSteps, "P.V hooks must fit");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
@@ -701,19 +701,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
             for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = __builtin_bit_cast(f16x8, *(const bf16x8*)(qrow + ks * 16));
         }
 
-        // first page of the segment, both batches, while the queries land
-        const Pieces pc = PiecesOf<kFp8>::make(opaque_lane(), wave);
-        const int phys0 = load_phys(p_lo);
-        const int phys1 = load_phys(p_lo + 1);
-        const __amdgpu_buffer_rsrc_t r0 = page_rsrc(p_lo, phys0);
-        Stage stg[kS], s0p[kPieces];
-        static_for<0, kPieces>([&](auto k) { pc.issue(s0p[k], r0, wave, k); });
-        __amdgpu_buffer_rsrc_t r_next = page_rsrc(p_lo + 1, phys1);
-        // block-table entries are loaded a tile before their use, so that
-        // reading them never waits on the loads issued after them
-        int phys2 = load_phys(p_lo + 2);
-
-        {
+        // scale each head's query by 2^-sh so its max |q| lands in [2^14, 2^15)
+        // and convert to fp16 (exact up to fp16 subnormals); the q_R part
+        // moves to LDS
+        auto convert_q = [&]() {
             float qmax = 0.f;
 #pragma unroll
             for (int ks = 0; ks < kKSteps; ++ks) {
@@ -738,9 +729,41 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
 #pragma unroll
             for (int ks = kQRegSteps; ks < kKSteps; ++ks)
                 *(LDS_AS f16x8*)(qr_lds + (ks - kQRegSteps) * 1024) = qf[ks];
-        }
+        };
         const f16x8(&qreg)[kQRegSteps] = *reinterpret_cast<const f16x8(*)[kQRegSteps]>(&qf[0]);
+        const Pieces pc = PiecesOf<kFp8>::make(opaque_lane(), wave);
 
+        // ---- Page pipeline, one barrier per tile.  Pieces stream through
+        // VGPRs (converted or dequantised in registers) into the idle
+        // tile: page p + 1 moves during tile p in three or four batches
+        // through one set of staging registers; each hook stores a batch
+        // (the first was issued during the previous tile) and issues the
+        // next; the last hook issues batch 0 of page p + 2.  Block-table
+        // entries are loaded a tile before their use.
+        typedef typename Pieces::Stage Stage;
+        constexpr int kNB = Pieces::kBatches;
+        constexpr int kS = Pieces::kStage;
+        static_assert(Pieces::first(kNB) == kPieces, "batches cover the page");
+        // the last hook issues page p + 2, whose descriptor exists after Q.K^T
+        static_assert(Pieces::kHookPv[kNB - 1] == 1, "the last hook must sit in P.V");
+        // slot k of hook h runs at step at(h) + k * stride(h) of its phase;
+        // hooks of one phase must not overlap and must fit their loop
+        static_for<0, kNB>([&](auto h_c) {
+            constexpr int h = decltype(h_c)::value;
+            constexpr int last = Pieces::kHookAt[h] + (kS - 1) * Pieces::kHookStride[h];
+            static_assert(last < (Pieces::kHookPv[h] ? kPvSteps : kKSteps), "hook must fit its loop");
+            if constexpr (h + 1 < kNB && Pieces::kHookPv[h + 1] == Pieces::kHookPv[h])
+                static_assert(last < Pieces::kHookAt[h + 1], "hooks of a phase must not overlap");
+        });
+
+        const int phys0 = load_phys(p_lo);
+        const int phys1 = load_phys(p_lo + 1);
+        const __amdgpu_buffer_rsrc_t r0 = page_rsrc(p_lo, phys0);
+        Stage stg[kS], s0p[kPieces];
+        static_for<0, kPieces>([&](auto k) { pc.issue(s0p[k], r0, wave, k); });
+        __amdgpu_buffer_rsrc_t r_next = page_rsrc(p_lo + 1, phys1);
+        int phys2 = load_phys(p_lo + 2);
+        convert_q();
         static_for<0, kPieces>([&](auto k) {
             pc.store(s0p[k], tiles[0], wave, k);
             if constexpr (k < Pieces::first(1)) pc.issue(stg[k], r_next, wave, k);   // batch 0 of page p_lo + 1
@@ -748,12 +771,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
         wg_barrier();
 
-        // Page pipeline, one barrier per tile.  During tile p (read from
-        // tiles[p & 1]) page p + 1 moves into the other tile in three or
-        // four batches through one set of staging registers: each hook
-        // stores a batch (the first one was issued during the previous
-        // tile) and issues the next; the last hook issues batch 0 of page
-        // p + 2.
         for (int p = p_lo; p < p_hi; ++p) {
             const LDS_AS uint8_t* tile = tiles[(p - p_lo) & 1];
             LDS_AS uint8_t* tnext = tiles[(p - p_lo + 1) & 1];
@@ -775,37 +792,32 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
             };
             auto qk_hook = [&](auto ks_c) {
                 constexpr int ks = decltype(ks_c)::value;
-                static_for<0, 2>([&](auto h_c) {
-                    constexpr int h = decltype(h_c)::value, at = Pieces::kQkHooks[h];
-                    if constexpr (ks >= at && (ks - at) % kQs == 0 && (ks - at) / kQs < kS)
-                        move_piece(std::integral_constant<int, h>{}, std::integral_constant<int, (ks - at) / kQs>{});
+                static_for<0, kNB>([&](auto h_c) {
+                    constexpr int h = decltype(h_c)::value, at = Pieces::kHookAt[h];
+                    constexpr int sd = Pieces::kHookStride[h];
+                    if constexpr (!Pieces::kHookPv[h] && ks >= at && (ks - at) % sd == 0 && (ks - at) / sd < kS)
+                        move_piece(h_c, std::integral_constant<int, (ks - at) / sd>{});
                 });
-                if constexpr (ks == kKSteps - 1) {
-                    r2 = page_rsrc(p + 2, phys2);
-                }
+                if constexpr (ks == kKSteps - 1) r2 = page_rsrc(p + 2, phys2);
             };
             auto pv_hook = [&](auto step_c) {
                 constexpr int step = decltype(step_c)::value;
-                static_for<0, kNPv>([&](auto h_c) {
-                    constexpr int h = decltype(h_c)::value, at = Pieces::kPvHooks[h];
-                    if constexpr (step >= at && (step - at) % kPs == 0 && (step - at) / kPs < kS)
-                        move_piece(std::integral_constant<int, h + 2>{},
-                                   std::integral_constant<int, (step - at) / kPs>{});
+                static_for<0, kNB>([&](auto h_c) {
+                    constexpr int h = decltype(h_c)::value, at = Pieces::kHookAt[h];
+                    constexpr int sd = Pieces::kHookStride[h];
+                    if constexpr (Pieces::kHookPv[h] && step >= at && (step - at) % sd == 0 && (step - at) / sd < kS)
+                        move_piece(h_c, std::integral_constant<int, (step - at) / sd>{});
                 });
-
             };
-            // inactive waves (rows beyond M) compute on row 0's query and
-            // discard the result: keeping the call unconditional keeps the
-            // accumulators out of control-flow merges
             compute_tile(tile, qreg, qr_lds, st, min(max(n_vis - p * kPage, 0), kPage), scale_lane, qk_hook,
                          pv_hook);
             r_next = r2;
             phys2 = phys_next;
-            __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);           // tile stores and reads retired
+            __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);       // tile stores and reads retired
             wg_barrier();
         }
-        // the last tiles issued loads of pages past p_hi: zero-size
-        // descriptors, nothing is fetched, and their registers are dead
+        // the last tile issued loads of pages past p_hi: zero-size
+        // descriptors, nothing is fetched, and they are never waited for
 
         // epilogue: normalise and write final output or the split's partial
         if (active) {
