@@ -688,12 +688,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         f16x8 qf[kKSteps];      // the q_R part moves to LDS after the conversion
         float scale_lane;
         WaveState st;
-        st.m = -__builtin_inff();
-        st.l = 0.f;
-        st.o_zero = true;
-#pragma unroll
-        for (int md = 0; md < kMdBlocks; ++md) st.o[md] = f32x16{};
         const int lane0 = tid & 63;
+        // segment prologue, ordered for overlap: the first block-table
+        // entries, then the queries; the first page is requested as soon as
+        // its entry lands and the query conversion runs under its latency
+        const int phys0 = load_phys(p_lo);
+        const int phys1 = load_phys(p_lo + 1);
         {
             const int row = active ? row0 + (lane0 & 31) : 0;
             const uint16_t* qrow = a.q + ((int64_t)b * M + row) * kD + (lane0 >> 5) * 8;
@@ -756,13 +756,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
                 static_assert(last < Pieces::kHookAt[h + 1], "hooks of a phase must not overlap");
         });
 
-        const int phys0 = load_phys(p_lo);
-        const int phys1 = load_phys(p_lo + 1);
         const __amdgpu_buffer_rsrc_t r0 = page_rsrc(p_lo, phys0);
         Stage stg[kS], s0p[kPieces];
         static_for<0, kPieces>([&](auto k) { pc.issue(s0p[k], r0, wave, k); });
         __amdgpu_buffer_rsrc_t r_next = page_rsrc(p_lo + 1, phys1);
         int phys2 = load_phys(p_lo + 2);
+        st.m = -__builtin_inff();
+        st.l = 0.f;
+        st.o_zero = true;
+#pragma unroll
+        for (int md = 0; md < kMdBlocks; ++md) st.o[md] = f32x16{};
         convert_q();
         static_for<0, kPieces>([&](auto k) {
             pc.store(s0p[k], tiles[0], wave, k);
