@@ -630,8 +630,20 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = a.num_workers;
-    const int worker = blockIdx.x % G;
-    const int rg = blockIdx.x / G;
+    // Workgroups are dealt to the 8 XCDs round robin (block i on XCD i % 8).
+    // When G is a multiple of 8 the row groups of one worker are given
+    // blocks on the same XCD, so they read each page through the same L2
+    // at about the same time and the cache is fetched from HBM once.
+    int worker, rg;
+    if (G % 8 == 0) {
+        const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+        const int R = (int)gridDim.x / G;
+        rg = j % R;
+        worker = (j / R) * 8 + xcd;
+    } else {
+        worker = blockIdx.x % G;
+        rg = blockIdx.x / G;
+    }
     const int M = a.s_q * a.n_h;
     const int row0 = rg * kRowsPerGroup + wave * kRowsPerWave;
     const bool active = row0 < M;
