@@ -35,8 +35,9 @@ FLOP_PER_ROW_TOKEN = 2 * 576 + 2 * 512   # Q.K^T over the 576-wide row + P.V ove
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first: the GPU needs ~20 ms of load to reach its steady clock")
     ap.add_argument("--workload", default=None, help="workload name (default: the long-context one)")
     ap.add_argument("--num-workers", type=int, default=0)
     ap.add_argument("--cpu-budget-s", type=float, default=15.0, help="oracle sample budget (seconds)")

@@ -32,7 +32,7 @@ struct mla_decode_handle {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kOverheadUnits = 2;    // per-segment cost of query load + epilogue, in pages
+constexpr int kOverheadUnits = 3;    // per-segment cost (query load, first page, epilogue), in pages: measured ~2.2 tiles of prologue plus the partial write
 constexpr int kMinQuota = 1;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }

@@ -702,16 +702,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         WaveState st;
         const int lane0 = tid & 63;
         // segment prologue, ordered for overlap: the first block-table
-        // entries, then the queries; the first page is requested as soon as
-        // its entry lands and the query conversion runs under its latency
+        // entries, then the first page as soon as its entry lands, then the
+        // queries; the page is stored while the queries are still arriving
+        // (loads complete in issue order), and the queries are converted after
         const int phys0 = load_phys(p_lo);
         const int phys1 = load_phys(p_lo + 1);
-        {
-            const int row = active ? row0 + (lane0 & 31) : 0;
-            const uint16_t* qrow = a.q + ((int64_t)b * M + row) * kD + (lane0 >> 5) * 8;
-#pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = __builtin_bit_cast(f16x8, *(const bf16x8*)(qrow + ks * 16));
-        }
 
         // scale each head's query by 2^-sh so its max |q| lands in [2^14, 2^15)
         // and convert to fp16 (exact up to fp16 subnormals); the q_R part
@@ -771,6 +766,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         const __amdgpu_buffer_rsrc_t r0 = page_rsrc(p_lo, phys0);
         Stage stg[kS], s0p[kPieces];
         static_for<0, kPieces>([&](auto k) { pc.issue(s0p[k], r0, wave, k); });
+        {
+            const int row = active ? row0 + (lane0 & 31) : 0;
+            const uint16_t* qrow = a.q + ((int64_t)b * M + row) * kD + (lane0 >> 5) * 8;
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = __builtin_bit_cast(f16x8, *(const bf16x8*)(qrow + ks * 16));
+        }
         __amdgpu_buffer_rsrc_t r_next = page_rsrc(p_lo + 1, phys1);
         int phys2 = load_phys(p_lo + 2);
         st.m = -__builtin_inff();
@@ -778,11 +779,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         st.o_zero = true;
 #pragma unroll
         for (int md = 0; md < kMdBlocks; ++md) st.o[md] = f32x16{};
-        convert_q();
         static_for<0, kPieces>([&](auto k) {
             pc.store(s0p[k], tiles[0], wave, k);
             if constexpr (k < Pieces::first(1)) pc.issue(stg[k], r_next, wave, k);   // batch 0 of page p_lo + 1
         });
+        convert_q();
         __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
         wg_barrier();
 
