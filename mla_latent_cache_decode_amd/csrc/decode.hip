@@ -338,17 +338,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base,
 // the piece is the contiguous 1 KiB at n * 1024 (see tile_off).
 struct Bf16Pieces {
     static constexpr int kPieces = 18;
-    // a page moves in five batches (pieces [0,4), [4,8), [8,12), [12,15),
-    // [15,18)).  Hook h stores batch h: its slot k runs in phase
-    // kHookPv[h] (0 = Q.K^T, 1 = P.V) at step kHookAt[h] + k * kHookStride[h].
-    // The hooks are spaced evenly in time over a tile (a Q.K^T step takes
-    // about twice a P.V step), so every batch gets the same time to land.
-    static constexpr int kBatches = 5;
-    static constexpr int kStage = 4;            // staging slots (largest batch)
-    __device__ static constexpr int first(int b) { return b <= 3 ? 4 * b : b == 4 ? 15 : 18; }
-    static constexpr int kHookPv[5] = {0, 0, 0, 1, 1};
-    static constexpr int kHookAt[5] = {0, 14, 28, 4, 34};
-    static constexpr int kHookStride[5] = {3, 3, 2, 6, 6};
+    // a page moves in three batches of six pieces.  Hook h stores batch h:
+    // its slot k runs in phase kHookPv[h] (0 = Q.K^T, 1 = P.V) at step
+    // kHookAt[h] + k * kHookStride[h]; the hooks are spread over the tile
+    // so that every batch has about a third of a tile to land.
+    static constexpr int kBatches = 3;
+    static constexpr int kStage = 6;            // staging slots (largest batch)
+    __device__ static constexpr int first(int b) { return 6 * b; }
+    static constexpr int kHookPv[3] = {0, 0, 1};
+    static constexpr int kHookAt[3] = {0, 18, 8};
+    static constexpr int kHookStride[3] = {2, 3, 8};
     typedef u32x4 Stage;
 
     int src_lane;       // (i >> 3) * 1152 + (i & 7) * 16
