@@ -3,7 +3,10 @@
 Two modes:
 
   stats    from a ``rocprofv3 --kernel-trace --stats --output-format csv`` run:
-           per-kernel call count and average / min / max duration.
+           per-kernel call count and average / min / max duration over all
+           calls, and (with --last N) the average over each kernel's last N
+           dispatches from the kernel trace: the timed steps of a bench run,
+           after its warm-up.
   traffic  from two ``rocprofv3 --pmc`` runs (FETCH_SIZE, then WRITE_SIZE;
            both in KiB per dispatch) of ``bench.py --copy-mb N``: the HBM
            bytes per dispatch of one kernel, each counter scaled by what it
@@ -58,16 +61,31 @@ def read_traffic(path: str) -> dict | None:
         return None
 
 
+def _short(name: str) -> str:
+    return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0][:60]
+
+
 def _stats(args) -> str:
     rows = list(csv.DictReader(open(args.csv)))
-    lines = [f"command: {args.command}", "", f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'min_us':>10} "
-             f"{'max_us':>10} {'pct':>6}"]
+    lines = [f"command: {args.command}", "", "all calls:",
+             f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
     for r in rows:
-        name = r["Name"]
-        short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0][:60]
-        lines.append(f"{short:<60} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+        lines.append(f"{_short(r['Name']):<60} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
                      f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
                      f"{float(r['Percentage']):>6.2f}")
+    if args.last:
+        trace = os.path.join(os.path.dirname(args.csv), os.path.basename(args.csv).replace("kernel_stats", "kernel_trace"))
+        per: dict[str, list[float]] = {}
+        for r in csv.DictReader(open(trace)):
+            per.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines += ["", f"last {args.last} dispatches of each kernel (the timed steps):",
+                  f"{'kernel':<60} {'n':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}"]
+        for name, ds in per.items():
+            d = ds[-args.last:]
+            if len(ds) < args.last:
+                continue
+            lines.append(f"{_short(name):<60} {len(d):>6} {statistics.mean(d):>10.2f} {min(d):>10.2f} {max(d):>10.2f}")
     return "\n".join(lines) + "\n"
 
 
@@ -123,6 +141,7 @@ def main(argv=None):
     s.add_argument("--csv", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
+    s.add_argument("--last", type=int, default=0, help="also average the last N dispatches per kernel")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
