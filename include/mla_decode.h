@@ -98,7 +98,7 @@ mla_status_t mla_decode_init(const mla_decode_params_t* params, mla_decode_handl
 /* mla_decode_workspace_size -- device workspace bytes that mla_decode_run needs
  * for `batch` sequences (0 <= batch <= max_batch).  `bytes` is a host pointer.
  * The workspace holds the per-call work plan and the split-KV partial results
- * (fp32 outputs and LSEs of every context split). */
+ * (fp16 normalised outputs and fp32 LSEs of every context split). */
 mla_status_t mla_decode_workspace_size(mla_decode_handle_t h, int32_t batch, size_t* bytes);
 
 /* mla_decode_run -- one decode step for `batch` sequences, all heads, all queries.

@@ -48,7 +48,7 @@ WsLayout layout(const mla_decode_handle* h, int32_t batch) {
     l.seq_nsplit = off;    off += align_up(nb * sizeof(int32_t));
     l.seq_slot = off;      off += align_up(nb * sizeof(int32_t));
     l.part_lse = off;      off += align_up((size_t)h->partial_slots * h->rows * sizeof(float));
-    l.part_o = off;        off += align_up((size_t)h->partial_slots * h->rows * mla::kDc * sizeof(float));
+    l.part_o = off;        off += align_up((size_t)h->partial_slots * h->rows * mla::kDc * sizeof(uint16_t));
     l.total = off;
     return l;
 }
@@ -194,7 +194,7 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     plan.seq_nsplit = (int32_t*)(ws + l.seq_nsplit);
     plan.seq_slot = (int32_t*)(ws + l.seq_slot);
     plan.part_lse = (float*)(ws + l.part_lse);
-    plan.part_o = (float*)(ws + l.part_o);
+    plan.part_o = (uint16_t*)(ws + l.part_o);
     hipStream_t stream = (hipStream_t)hip_stream;
 
     mla::DecodeArgs da;

@@ -1,0 +1,291 @@
+// Device code shared by the decode kernels: types, the LDS tile swizzle,
+// lane-pair reductions, the work plan and buffer descriptors.
+#pragma once
+
+#include "mla_internal.h"
+
+#include <type_traits>
+#include <utility>
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+#define LDS_AS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
+
+constexpr int kChunks = kD / 8;                 // 72 chunks of 8 halves (16 B) per row
+constexpr int kTileBytes = kPage * kD * 2;      // 73728: one page of 16-bit elements
+constexpr int kKSteps = kD / 16;                // 36 MFMA k-steps for Q.K^T
+constexpr int kMdBlocks = kDc / 32;             // 16 output blocks of 32 dims
+
+static_assert(kChunks % 8 == 0, "row must be whole 64-dim column blocks");
+
+#define LGKMCNT0_IMM 0xC07F
+#define VMCNT0_IMM 0x0F70
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Read-only per-call metadata (block table, lengths) is read through the
+// constant address space so the loads are scalar (SMEM): a vector load here
+// would have to wait on vmcnt, which also counts the in-flight page loads.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p) {
+    return *(const CONST_AS T*)p;
+}
+
+// Slot swizzle of token t: bits (t1, t2, t3) of t become slot bits (2, 1, 0).
+// LDS serves 16 lanes of a 128-bit access per pass over 64 banks.  A row
+// read of 16 consecutive tokens (Q.K^T fragments, fp8 stores) then hits 16
+// distinct 16-byte slots: even tokens cover slots 0..7 of the 256-byte bank
+// window, odd tokens 8..15, each through a bijection of (t1, t2, t3).  The
+// transposed PV reads touch tokens T, T+1, T+2, T+3 (T = 0 mod 4) in four
+// adjacent chunks; slot bit 2 = t1 separates T from T+2 (and T+1 from T+3).
+__device__ __forceinline__ int sw(int t) { return (((t >> 1) & 1) << 2) | (((t >> 2) & 1) << 1) | ((t >> 3) & 1); }
+
+// byte offset of (token t, chunk c) inside a tile (16-bit elements)
+__device__ __forceinline__ int tile_off(int t, int c) {
+    return (((c >> 3) << 9) + (t << 3) + ((c & 7) ^ sw(t))) << 4;
+}
+
+// Lanes l and l^32 hold the two halves of one head's tokens.  permlane32_swap
+// with both operands = v returns (v[l % 32], v[l % 32 + 32]) in some order, so
+// a symmetric combination of the pair is the head-wide reduction.
+__device__ __forceinline__ float pair_max(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                              __builtin_bit_cast(uint32_t, v), false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                              __builtin_bit_cast(uint32_t, v), false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Workgroup barrier without a memory fence: a fence would make the compiler
+// wait for every in-flight page load as well.
+// Callers wait for exactly what they need (s_waitcnt) before it; the empty
+// asm statements stop the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x * alpha for an accumulator element that lives in an AGPR.  Written as
+// asm so the 256-register O accumulator keeps AGPRs as its home: a plain
+// VALU multiply would make the register allocator move all of O into arch
+// VGPRs and spill.  Only the (rare) lazy-rescale path uses it; the last MFMA
+// that wrote x is a whole tile (>= 72 MFMAs) earlier and the next MFMA that
+// reads it is behind the softmax, so no extra wait states are needed.
+__device__ __forceinline__ float scale_acc(float x, float alpha) {
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp)
+                 : "v"(alpha));
+    return x;
+}
+
+// The lane id, hidden from loop-invariant code motion.  Lane-derived
+// offsets are recomputed from it per tile (a handful of VALU ops) instead of
+// being hoisted out of the page loop, where they would occupy registers for
+// the whole kernel and push the register allocator into spilling.
+__device__ __forceinline__ int opaque_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// A copy of a lane value that the compiler must materialise where it is
+// used: offsets derived from it are then computed next to their load instead
+// of being hoisted out of the page loop (18 live offsets would spill).
+__device__ __forceinline__ int pinned(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// work plan
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+// Exclusive scan of two ints over the 256 threads, with the totals.
+__device__ __forceinline__ void block_scan2(int& a, int& b, int& ta, int& tb, int* sbuf, int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+    const int ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
+    __syncthreads();
+    if (lane == 63) {
+        sbuf[wave * 2 + 0] = ia;
+        sbuf[wave * 2 + 1] = ib;
+    }
+    __syncthreads();
+    int pa = 0, pb = 0;
+    ta = tb = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave) {
+            pa += sbuf[w * 2 + 0];
+            pb += sbuf[w * 2 + 1];
+        }
+        ta += sbuf[w * 2 + 0];
+        tb += sbuf[w * 2 + 1];
+    }
+    a = pa + ia - a;
+    b = pb + ib - b;
+}
+
+struct WorkerStart {
+    int b;          // first sequence this worker serves (batch if none)
+    int64_t cost;   // cost-axis position where sequence b starts
+    int slot;       // first partial slot of sequence b
+    int64_t quota;  // cost units per worker
+};
+
+// The worker's starting point on the cost axis.  With write_info it also
+// records, for every sequence whose cost position lies in this worker's
+// quota, the number of segments it is split into and its first partial slot
+// (read by the combine); only the first row group does that.
+__device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_info, int* sbuf, int tid) {
+    const int B = a.batch, G = a.num_workers, c = a.overhead_units;
+    int t_cost = 0;
+    const int my_len = tid < B ? a.seq_lens[tid] : 0;      // reused by the first chunk
+    {
+        int local = my_len > 0 ? (my_len + kPage - 1) / kPage + c : 0, zero = 0, tz;
+        for (int b = tid + kDecodeThreads; b < B; b += kDecodeThreads) {
+            const int L = a.seq_lens[b];
+            local += L > 0 ? (L + kPage - 1) / kPage + c : 0;
+        }
+        block_scan2(local, zero, t_cost, tz, sbuf, tid);
+    }
+    const int64_t Q = max(max(((int64_t)t_cost + G - 1) / G, (int64_t)a.min_quota), (int64_t)1);
+    const int64_t w_lo = (int64_t)worker * Q, w_hi = w_lo + Q;
+
+    WorkerStart ws;
+    ws.b = B;
+    ws.cost = 0;
+    ws.slot = 0;
+    ws.quota = Q;
+    int64_t carry_cost = 0;
+    int carry_slot = 0;
+    for (int base = 0; base < B; base += kDecodeThreads) {
+        const int b = base + tid;
+        int pages = 0;
+        if (b < B) {
+            const int L = base == 0 ? my_len : a.seq_lens[b];
+            pages = L > 0 ? (L + kPage - 1) / kPage : 0;
+        }
+        // a sequence's segment count depends on its cost prefix, so two scans
+        int cost_ex = pages > 0 ? pages + c : 0, zero = 0, tc, tz;
+        block_scan2(cost_ex, zero, tc, tz, sbuf, tid);
+        const int64_t C = carry_cost + cost_ex;
+        const int64_t A = C + c, E = A + pages;
+        const int n = pages > 0 ? (int)((E - 1) / Q - A / Q + 1) : 0;
+        int slot_ex = n > 1 ? n : 0, zero2 = 0, ts, tz2;
+        block_scan2(slot_ex, zero2, ts, tz2, sbuf, tid);
+        const int slot = carry_slot + slot_ex;
+        if (write_info && b < B) {
+            const int64_t owner = pages > 0 ? A / Q : min(C / Q, (int64_t)G - 1);
+            if (owner == worker) {
+                a.plan.seq_nsplit[b] = n;
+                a.plan.seq_slot[b] = slot;
+            }
+        }
+        if (ws.b == B) {
+            // first sequence of this chunk whose pages reach past w_lo
+            const bool cand = b < B && pages > 0 && E > w_lo;
+            const unsigned long long m = __builtin_amdgcn_ballot_w64(cand);
+            __syncthreads();
+            if ((tid & 63) == 0) sbuf[8 + (tid >> 6)] = m ? (int)__builtin_ctzll(m) + (tid & ~63) : kDecodeThreads;
+            __syncthreads();
+            int first = kDecodeThreads;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) first = min(first, sbuf[8 + w]);
+            if (first < kDecodeThreads) {
+                __syncthreads();
+                if (tid == first) {
+                    sbuf[12] = (int)(C & 0x3FFFFFFF);
+                    sbuf[13] = (int)(C >> 30);
+                    sbuf[14] = slot;
+                }
+                __syncthreads();
+                ws.b = base + first;
+                ws.cost = ((int64_t)sbuf[13] << 30) | (int64_t)sbuf[12];
+                ws.slot = sbuf[14];
+            }
+        }
+        carry_cost += tc;
+        carry_slot += ts;
+        // stop once past this worker's quota (sequences owned by it are then done too)
+        if (carry_cost >= w_hi) break;
+    }
+    __syncthreads();
+    return ws;
+}
+
+// Buffer descriptor over [base, base + bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int bytes) {
+    // both inputs are wave-uniform; say so, or the compiler wraps each load
+    // in a waterfall loop
+    const uint64_t b = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint8_t* ub = (const uint8_t*)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0, __builtin_amdgcn_readfirstlane(bytes),
+                                             0x00020000);
+}
+
+// Four consecutive dims of a split's normalised partial output as fp16.
+// O / l is a weighted mean of cache values that already passed through fp16
+// for the P.V product, so it is inside the fp16 range; the rounding (2^-11
+// relative) is far below the output tolerance and halves the bytes the
+// split writes and the combine reads.
+__device__ __forceinline__ void store_partial4(uint16_t* dst, f32x4 v) {
+    const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *(u32x2*)dst = __builtin_bit_cast(u32x2, h);
+}
+
+// Workgroups are dealt to the 8 XCDs round robin (block i on XCD i % 8).
+// When the worker count G is a multiple of 8 the row groups of one worker
+// are given blocks on the same XCD, so they read each page through the same
+// L2 at about the same time and the cache is fetched from HBM once.
+__device__ __forceinline__ void block_role(int G, int& worker, int& rg) {
+    if (G % 8 == 0) {
+        const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+        const int R = (int)gridDim.x / G;
+        rg = j % R;
+        worker = (j / R) * 8 + xcd;
+    } else {
+        worker = blockIdx.x % G;
+        rg = blockIdx.x / G;
+    }
+}
+
+}  // namespace
+}  // namespace mla

@@ -31,7 +31,7 @@ struct PlanView {
     int32_t* seq_nsplit;        // [batch]
     int32_t* seq_slot;          // [batch]
     float* part_lse;            // [slots][M]
-    float* part_o;              // [slots][M][kDc]
+    uint16_t* part_o;           // fp16 [slots][M][kDc]: a split's O / l
 };
 
 struct DecodeArgs {

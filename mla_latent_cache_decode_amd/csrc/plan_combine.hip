@@ -3,7 +3,7 @@
 // The log-sum-exp merge of a sequence's partial results,
 //     lse = log sum_i exp(lse_i),   out = sum_i exp(lse_i - lse) * out_i,
 // which is exact because each partial out_i is already normalised by its own
-// softmax denominator.  The decode kernel records, per sequence, how many
+// softmax denominator (the partials are stored as fp16, the sums are fp32).  The decode kernel records, per sequence, how many
 // splits it produced and where its partial slots start; a sequence served
 // by a single worker was finished by the decode kernel and is skipped here.
 #include "mla_internal.h"
@@ -12,6 +12,7 @@ namespace mla {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCombineRows = 2;          // query rows per block, 128 threads x 4 dims each
 constexpr int kUnroll = 8;               // partial loads in flight per thread
@@ -72,18 +73,23 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
     sum = s_red[r][0] + s_red[r][1];
     const float inv = 1.0f / sum;
-    const float* src = a.plan.part_o + ((int64_t)base * M + row) * kDc + t * 4;
+    // partials are fp16 (see the decode epilogue), four dims per thread
+    const uint16_t* src = a.plan.part_o + ((int64_t)base * M + row) * kDc + t * 4;
     const int64_t stride = (int64_t)M * kDc;
+    auto load4 = [&](int i) -> f32x4 {
+        const f16x4 h = *(const f16x4*)(src + i * stride);
+        return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     int i = 0;
     for (; i + kUnroll <= n; i += kUnroll) {
         f32x4 v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = *(const f32x4*)(src + (i + u) * stride);
+        for (int u = 0; u < kUnroll; ++u) v[u] = load4(i + u);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc += s_w[r][i + u] * v[u];
     }
-    for (; i < n; ++i) acc += s_w[r][i] * *(const f32x4*)(src + i * stride);
+    for (; i < n; ++i) acc += s_w[r][i] * load4(i);
     *o = acc * inv;
     if (a.lse && t == 0) a.lse[(int64_t)b * M + row] = mx + logf(sum);
 }

@@ -169,3 +169,42 @@ def test_batch_zero_is_a_noop_and_errors_are_reported():
                               ws.numel(), None) == m.MLA_ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
     assert torch.count_nonzero(out).item() == 0
+
+
+def _scale_later_tokens(w, start: int, log2_factor: int):
+    """Scale every cached element of logical tokens >= start by 2^log2_factor,
+    exactly: bf16 exponent field + k, or each fp8 row's e8m0 scale bytes + k.
+    Scores against those tokens grow by the same factor, so a later block's
+    max exceeds the first block's by far more than the lazy-max threshold."""
+    pool2 = w.pool.copy()
+    for b in range(w.spec.batch):
+        for t in range(start, int(w.seq_lens[b])):
+            pg, r = w.block_table[b, t // 64], t % 64
+            if w.spec.kv_dtype == "bf16":
+                row = pool2[pg, r].astype(np.int32)
+                e = (row >> 7) & 0xFF
+                nz = e != 0
+                row[nz] += log2_factor << 7
+                pool2[pg, r] = row.astype(np.uint16)
+            else:
+                d = w.spec.d
+                pool2[pg, r, d:d + d // 32] += np.uint8(log2_factor)
+    return dataclasses.replace(w, pool=pool2)
+
+
+RISING = [
+    WorkloadSpec("rising_bf16", 3, ("fixed", (700, 2000, 4100)), spare_pages=4, seed=21),
+    WorkloadSpec("rising_mtp", 2, ("fixed", (900, 3000)), s_q=2, spare_pages=4, seed=22),
+    WorkloadSpec("rising_fp8", 3, ("fixed", (700, 2000, 4100)), kv_dtype="fp8", spare_pages=4, seed=23),
+]
+
+
+@pytest.mark.parametrize("spec", RISING, ids=[s.name for s in RISING])
+@pytest.mark.parametrize("workers", [0, 1, 7])
+def test_rising_scores(spec, workers):
+    # the softmax max of a segment moves up by ~8x mid-way: the kernels'
+    # lazily kept max must still give the oracle's result
+    w = _scale_later_tokens(make_workload(spec), start=300, log2_factor=3)
+    out, lse = run_gpu(w, num_workers=workers)
+    ro, rl = oracle(w)
+    assert_parity(w, out, lse, ro, rl)
