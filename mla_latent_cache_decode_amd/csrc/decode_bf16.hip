@@ -439,24 +439,89 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
                     a.plan.part_lse[(int64_t)slot * M + row] = lse_v;
                 }
             }
-            const int hi = lane >> 5;
+            // O^T lives in MFMA layout (lane = row), so direct stores would
+            // scatter 8-16 bytes over 32 rows per instruction.  The rows go
+            // through LDS (the tile buffers are free) and leave as whole rows.
+            // lane-derived offsets come from opaque_lane() so that they are
+            // computed here, not hoisted out of the page loop into registers
+            const int lane_e = opaque_lane();
+            const int hi = lane_e >> 5;
+            float inv[4];
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb) {
-                if (hb < n_blocks) {
-                    const float inv = inv_l[hb * 32 + (lane & 31)];
-                    const int row = row_base + hb * 32 + (lane & 31);
-                    const int col = wave * 128 + hi * 4;
-                    float* dst = a.out + ((int64_t)b * M + row) * kDc + col;
-                    uint16_t* pdst = a.plan.part_o + ((int64_t)(slot < 0 ? 0 : slot) * M + row) * kDc + col;
+            for (int hb = 0; hb < 4; ++hb) inv[hb] = inv_l[hb * 32 + (lane_e & 31)];
+            auto norm4 = [&](int db, int hb, int r4) {
+                return f32x4{o[db][hb][r4 * 4 + 0] * inv[hb], o[db][hb][r4 * 4 + 1] * inv[hb],
+                             o[db][hb][r4 * 4 + 2] * inv[hb], o[db][hb][r4 * 4 + 3] * inv[hb]};
+            };
+            const int n_rows = n_blocks * kRowsPerWave;
+            if (slot >= 0) {
+                // fp16 partial rows of 1 KiB; 8-byte slot s of row r sits at
+                // slot s ^ (r & 31), so the 32 rows one write touches hit
+                // distinct banks
 #pragma unroll
-                    for (int db = 0; db < 4; ++db) {
+                for (int hb = 0; hb < 4; ++hb) {
+                    if (hb < n_blocks) {
+                        const int r = hb * 32 + (lane_e & 31);
 #pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) {
-                            f32x4 v = {o[db][hb][r4 * 4 + 0] * inv, o[db][hb][r4 * 4 + 1] * inv,
-                                       o[db][hb][r4 * 4 + 2] * inv, o[db][hb][r4 * 4 + 3] * inv};
-                            if (slot < 0) *(f32x4*)(dst + db * 32 + r4 * 8) = v;
-                            else store_partial4(pdst + db * 32 + r4 * 8, v);
+                        for (int db = 0; db < 4; ++db)
+#pragma unroll
+                            for (int r4 = 0; r4 < 4; ++r4) {
+                                const f32x4 v = norm4(db, hb, r4);
+                                const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                                const int sl = wave * 32 + db * 8 + r4 * 2 + hi;
+                                *(LDS_AS u32x2*)(lds + r * 1024 + ((sl ^ (r & 31)) << 3)) = __builtin_bit_cast(u32x2, h);
+                            }
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
+                wg_barrier();
+                // wave w stores rows 32w .. 32w + 31, lane l the 16 bytes of
+                // logical slots 2l, 2l + 1
+                uint16_t* const pbase = a.plan.part_o + ((int64_t)slot * M + row_base) * kDc + lane_e * 8;
+                for (int j = 0; j < kRowsPerWave; ++j) {
+                    const int r = wave * kRowsPerWave + j;
+                    if (r >= n_rows) break;
+                    u32x4 v = *(const LDS_AS u32x4*)(lds + r * 1024 + (((2 * lane_e) ^ (r & 30)) << 3));
+                    if (r & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+                    *(u32x4*)(pbase + r * kDc) = v;
+                }
+            } else {
+                // fp32 output rows of 2 KiB, 64 rows at a time; 16-byte
+                // granule g of row r sits at granule g ^ (r & 15)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int hb = 2 * half + hh;
+                        if (hb < n_blocks) {
+                            const int r = hh * 32 + (lane_e & 31);
+#pragma unroll
+                            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                                for (int r4 = 0; r4 < 4; ++r4) {
+                                    const int g = wave * 32 + db * 8 + r4 * 2 + hi;
+                                    *(LDS_AS f32x4*)(lds + r * 2048 + ((g ^ (r & 15)) << 4)) = norm4(db, hb, r4);
+                                }
                         }
+                    }
+                    __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
+                    wg_barrier();
+                    // wave w stores rows 16w .. 16w + 15 of the half, two
+                    // instructions of 1 KiB per row
+                    float* const obase = a.out + ((int64_t)b * M + row_base + half * 64) * kDc + lane_e * 4;
+                    for (int j = 0; j < 16; ++j) {
+                        const int r = wave * 16 + j;
+                        if (half * 64 + r >= n_rows) break;
+#pragma unroll
+                        for (int k = 0; k < 2; ++k) {
+                            const int g = k * 64 + lane_e;
+                            const f32x4 v = *(const LDS_AS f32x4*)(lds + r * 2048 + ((g ^ (r & 15)) << 4));
+                            *(f32x4*)(obase + r * kDc + k * 256) = v;
+                        }
+                    }
+                    if (half == 0) {
+                        __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
+                        wg_barrier();
                     }
                 }
             }
