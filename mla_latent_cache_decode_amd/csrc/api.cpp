@@ -227,7 +227,7 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     ca.lse = lse;
     ca.batch = batch;
     ca.rows = h->rows;
-    if (mla::launch_combine(ca, stream) != hipSuccess) return MLA_ERR_HIP;
+    if (mla::launch_combine(ca, h->num_workers, stream) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
 

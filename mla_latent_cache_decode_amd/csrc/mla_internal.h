@@ -64,6 +64,8 @@ struct CombineArgs {
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream);
-hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+// max_splits: an upper bound on the splits of one sequence (the worker
+// count); it sizes the combine's LDS and picks its shape.
+hipError_t launch_combine(const CombineArgs& a, int max_splits, hipStream_t stream);
 
 }  // namespace mla
