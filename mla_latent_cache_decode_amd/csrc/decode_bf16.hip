@@ -171,15 +171,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             dma16(r, (pinned(dma_lane) ^ ((k & 1) << 4)) + off, (uint32_t)(uintptr_t)(tile + pn * 1024));
         };
 
-        // this wave's 32 query rows as bf16 B-operands: lane i holds row
-        // i & 31, elements 8 (i >> 5) .. + 7 of each 16-element k-step
-        bf16x8 qf[kKSteps];
-        {
-            const int row = active ? row0 + (lane0 & 31) : 0;
-            const uint16_t* qrow = a.q + ((int64_t)b * M + row) * kD + (lane0 >> 5) * 8;
-#pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8*)(qrow + ks * 16);
-        }
         const float scale_log2 = a.scale_log2;
         RowState rs;
         rs.m = -__builtin_inff();
@@ -191,6 +182,17 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             const __amdgpu_buffer_rsrc_t r0 = page_rsrc(p_lo, phys0);
 #pragma unroll
             for (int k = 0; k < kDmaPerWave; ++k) dma_piece(r0, tiles[0], k);
+        }
+        // this wave's 32 query rows as bf16 B-operands: lane i holds row
+        // i & 31, elements 8 (i >> 5) .. + 7 of each 16-element k-step.
+        // Loaded per pass (from L2 on a second pass) so that they are not
+        // live across the epilogue.
+        bf16x8 qf[kKSteps];
+        {
+            const int row = active ? row0 + (lane0 & 31) : 0;
+            const uint16_t* qrow = a.q + ((int64_t)b * M + row) * kD + (lane0 >> 5) * 8;
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8*)(qrow + ks * 16);
         }
         rs.l = 0.f;
         bool overflow = false;
@@ -429,10 +431,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
         wg_barrier();
         const bool again = pass == 0 && (flags[0] | flags[1] | flags[2] | flags[3]);
         if (!again) {
-            if (lane < 32 && active) {
+            // lane-derived offsets come from opaque_lane() so that they are
+            // computed here, not hoisted out of the page loop into registers
+            const int lane_e = opaque_lane();
+            if (lane_e < 32 && active) {
                 const float lse_v = l_tot > 0.f ? (rs.m + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
                                                 : -__builtin_inff();
-                const int row = row0 + lane;
+                const int row = row0 + lane_e;
                 if (slot < 0) {
                     if (a.lse) a.lse[(int64_t)b * M + row] = lse_v;
                 } else {
@@ -442,9 +447,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             // O^T lives in MFMA layout (lane = row), so direct stores would
             // scatter 8-16 bytes over 32 rows per instruction.  The rows go
             // through LDS (the tile buffers are free) and leave as whole rows.
-            // lane-derived offsets come from opaque_lane() so that they are
-            // computed here, not hoisted out of the page loop into registers
-            const int lane_e = opaque_lane();
             const int hi = lane_e >> 5;
             float inv[4];
 #pragma unroll
@@ -470,6 +472,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
                                 const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
                                 const int sl = wave * 32 + db * 8 + r4 * 2 + hi;
                                 *(LDS_AS u32x2*)(lds + r * 1024 + ((sl ^ (r & 31)) << 3)) = __builtin_bit_cast(u32x2, h);
+                                // one accumulator block at a time
+                                __builtin_amdgcn_sched_barrier(0);
                             }
                     }
                 }
@@ -501,6 +505,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
                                 for (int r4 = 0; r4 < 4; ++r4) {
                                     const int g = wave * 32 + db * 8 + r4 * 2 + hi;
                                     *(LDS_AS f32x4*)(lds + r * 2048 + ((g ^ (r & 15)) << 4)) = norm4(db, hb, r4);
+                                    __builtin_amdgcn_sched_barrier(0);
                                 }
                         }
                     }
