@@ -87,12 +87,12 @@ def cpu_baseline(w, budget_s: float) -> dict:
                       f"float64 numpy oracle, {dt:.2f} s wall"}
 
 
-def measured_traffic(workload: str) -> dict | None:
+def measured_traffic(kernel: str, workload: str) -> dict | None:
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
     if it was taken on this workload and on the kernel source as it is now."""
     from mla_latent_cache_decode_amd.rocprof_summary import kernel_source_hash, read_traffic
-    t = read_traffic(os.path.join(ROOT, "profiles", f"mla_decode_kernel_{workload}_traffic.txt"))
-    if t is None or t["source_hash"] != kernel_source_hash():
+    t = read_traffic(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt"))
+    if t is None or t["source_hash"] != kernel_source_hash(kernel):
         return None
     return t
 
@@ -172,7 +172,9 @@ def main():
     tflops = fl / (ms_step * 1e-3) / 1e12
     k_gbs = kv_bytes / (kms * 1e-3) / 1e9
     info = dec.info()
-    traffic = measured_traffic(s.name)
+    from mla_latent_cache_decode_amd.rocprof_summary import kernel_for_dtype
+    kernel = kernel_for_dtype(s.kv_dtype)
+    traffic = measured_traffic(kernel, s.name)
     res = {
         "metric": "MLA decode KV-read GB/s (% of HBM peak) + TFLOP/s, n_h=128, 1 GPU",
         "value": round(gbs, 2),
@@ -198,7 +200,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
-                     "kernel": "mla_decode_kernel", "kernel_ms": round(kms, 5),
+                     "kernel": kernel, "kernel_ms": round(kms, 5),
                      "bytes_per_launch": kv_bytes},
     }
     if not args.no_cpu_baseline:

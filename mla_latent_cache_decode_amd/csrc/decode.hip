@@ -1,4 +1,5 @@
-// Split-KV MLA decode kernels for gfx950 (CDNA4).
+// Split-KV MLA decode for an fp8 latent cache (e4m3 codes + one e8m0 scale
+// per 32) on gfx950 (CDNA4).
 //
 // What one workgroup computes ("DeepSeek R1 Architecture & Deployment Guide",
 // section 1.1): for 128 query rows (heads of one or more query positions) and
@@ -6,47 +7,35 @@
 //     S = K Q^T      over the 576-element shared row (latent c, then RoPE k_R),
 //     online softmax of S over the tokens,
 //     O = V^T P^T    with V = the first 512 elements (the latent c) of the
-//                    same rows, since the value up-projection is absorbed
-//                    into the output projection downstream.
-// Partial results (O/l, lse) of a split go to the workspace for the LSE
-// combine; a sequence served by one worker is finished here directly.
+//                    same rows (the value up-projection is absorbed into the
+//                    output projection downstream).
+// A split's partial result (O / l, lse) goes to the workspace for the LSE
+// combine; a sequence served by one worker is finished here directly.  The
+// row format (codes over every dimension, RoPE included, then one e8m0 scale
+// per 32 codes) is the "DeepSeek-R1" record's engine constraint (2).
 //
-// Mapping onto CDNA4:
-//  * Work plan.  Every workgroup derives its own share from seq_lens: the
-//    batch's pages are laid end to end on a cost axis (each sequence charged
-//    a fixed overhead for its query load and epilogue) and cut into
-//    num_workers equal quotas.  A (worker, sequence) overlap is a segment.
-//    No separate planning launch, no host round trip.
-//  * 4 waves x 32 rows.  Each wave holds its 32 query rows as MFMA B-operands
-//    in registers (36 k-steps x 8 halves) and its O^T accumulator (512 x 32
-//    fp32, 256 AGPRs).  Heads are the MFMA N dimension in both products, so
-//    softmax statistics of a head live in one lane pair (l, l^32) and the S^T
-//    accumulator is directly the B-operand of the PV product.
-//  * One 64-token page is one tile.  The workgroup copies it HBM->LDS with
-//    buffer loads straight into LDS (no VGPR staging), double buffered, and
-//    every wave reuses it for all of its heads: the cache is read from HBM
-//    once per workgroup.  Rows past the visible tokens are never fetched (the
-//    descriptor size excludes them; the LDS receives zeros).
+// Mapping onto CDNA4 (one workgroup of 4 waves per CU):
+//  * 4 waves x 32 rows.  Each wave holds its 32 query rows as fp16 MFMA
+//    B-operands (q_abs in VGPRs, q_R in LDS) and its O^T accumulator (512 x
+//    32 fp32, 256 AGPRs).  Heads are the MFMA N dimension in both products,
+//    so a head's softmax statistics live in one lane pair (l, l^32) and the
+//    S^T accumulator is directly the B-operand of the PV product.
+//  * One 64-token page is one tile.  Page p + 1 streams through VGPRs while
+//    tile p is computed: 16-byte buffer loads of codes and their scale byte,
+//    dequantised in registers (v_cvt_scalef32_pk_f16_fp8) and stored into
+//    the idle fp16 LDS tile by hooks placed between the MFMA steps; one
+//    barrier per tile.  Rows past the visible tokens are never fetched (the
+//    descriptor size excludes them; the tile receives zeros).
 //  * LDS tile layout: 9 column blocks of 64 dims; within a block, token t's
-//    16-byte chunk c sits at slot t*8 + (c ^ sw(t)).  The swizzle keeps the
-//    row-wise 128-bit reads of Q.K^T and the transposed 64-bit reads of the
-//    PV operand (ds_read_b64_tr_b16) free of bank conflicts.
-//  * Both products run as fp16 MFMA with fp32 accumulation.  A landed bf16
-//    page is converted to fp16 in place, once per workgroup (exact for
-//    values inside the fp16 range: bf16 carries fewer significand bits).
-//    fp16 matters for P: its rounding error is 8x below bf16's, which keeps
-//    the softmax weights accurate even when the reference max is stale.
+//    16-byte chunk c sits at slot t*8 + (c ^ sw(t)), conflict-free for the
+//    row-wise Q.K^T reads, the dequantised stores and the transposed PV
+//    reads (ds_read_b64_tr_b16).
+//  * Both products run as fp16 MFMA with fp32 accumulation; queries are
+//    prescaled per head by a power of two into [2^14, 2^15) before the fp16
+//    conversion (exact) and the factor is folded into the softmax scale.
 //  * Lazy rescaling: the running max is only raised when a tile's max
-//    exceeds it by more than 2^15 (in exp2 units), so O is rarely rescaled
-//    after the first tile; exponentials stay <= 2^15, inside fp16 range.
-//  * Queries are scaled per head by a power of two into [2^14, 2^15) before
-//    the fp16 conversion (exact), and the factor is folded into that head's
-//    softmax scale, so any query magnitude is representable.
-//  * FP8 pages (e4m3 codes + e8m0 per 32) land in an LDS staging buffer and
-//    are dequantised once per workgroup into the same fp16 tile layout
-//    (exact for values inside the fp16 range).
-//  * Operand fragments are read from LDS two MFMA steps ahead of use; the
-//    step order is pinned with scheduling barriers.
+//    exceeds it by more than 15 (log2 units), so O is rarely rescaled after
+//    the first tile and the exponentials stay <= 2^15, inside fp16 range.
 #include "decode_common.h"
 
 namespace mla {
@@ -65,12 +54,11 @@ constexpr int kQLdsBytes = 4 * kQLdsSteps * 1024;  // 16384: 4 waves x 4 fragmen
 constexpr int kLdsBytes = kLdsTiles + kQLdsBytes;  // 163840 = all of a CU's LDS
 
 // ---------------------------------------------------------------------------
-// page pieces: HBM -> VGPRs -> (convert / dequantise) -> fp16 LDS tile
+// page pieces: HBM -> VGPRs -> dequantise -> fp16 LDS tile
 // ---------------------------------------------------------------------------
 //
 // A page is moved by the four waves in pieces of one 16-byte vector load
-// per lane (1 KiB of bf16 per wave, or 16 fp8 codes plus their scale byte
-// per lane).  A piece is issued into registers well ahead of its use and
+// per lane (16 fp8 codes, plus their scale byte).  A piece is issued into registers well ahead of its use and
 // stored into the tile that the next tile step reads; both halves of the
 // work are spread over the MFMA steps of the current tile, so the memory
 // path, the conversion and the matrix cores overlap.
@@ -79,55 +67,6 @@ constexpr int kLdsBytes = kLdsTiles + kQLdsBytes;  // 163840 = all of a CU's LDS
 // is n_valid rows: lanes whose row lies past the visible tokens read zeros
 // (the rows are never fetched) and the tile receives finite zeros.  The
 // whole offset of a lane is in the VGPR offset, so the range check sees it.
-
-// bf16 rows.  Wave w moves pieces n = 18w + k, k < 18.  Piece n covers the
-// 64-dim column block n >> 3 of tokens 8(n & 7) .. 8(n & 7) + 7: lane i
-// carries token 8(n & 7) + (i >> 3), chunk 8(n >> 3) + (i & 7).  In the tile
-// the piece is the contiguous 1 KiB at n * 1024 (see tile_off).
-struct Bf16Pieces {
-    static constexpr int kPieces = 18;
-    // a page moves in three batches of six pieces.  Hook h stores batch h:
-    // its slot k runs in phase kHookPv[h] (0 = Q.K^T, 1 = P.V) at step
-    // kHookAt[h] + k * kHookStride[h]; the hooks are spread over the tile
-    // so that every batch has about a third of a tile to land.
-    static constexpr int kBatches = 3;
-    static constexpr int kStage = 6;            // staging slots (largest batch)
-    __device__ static constexpr int first(int b) { return 6 * b; }
-    static constexpr int kHookPv[3] = {0, 0, 1};
-    static constexpr int kHookAt[3] = {0, 18, 8};
-    static constexpr int kHookStride[3] = {2, 3, 8};
-    typedef u32x4 Stage;
-
-    int src_lane;       // (i >> 3) * 1152 + (i & 7) * 16
-    int dst_lane;       // tile_off(i >> 3, i & 7)
-
-    __device__ __forceinline__ explicit Bf16Pieces(int lane) {
-        src_lane = (lane >> 3) * kBf16RowBytes + ((lane & 7) << 4);
-        dst_lane = tile_off(lane >> 3, lane & 7);
-    }
-    __device__ __forceinline__ static int piece(int wave, int k) { return wave * kPieces + k; }
-
-    __device__ __forceinline__ void issue(Stage& s, __amdgpu_buffer_rsrc_t r, int wave, int k) const {
-        const int n = piece(wave, k);
-        const int off = (n & 7) * 8 * kBf16RowBytes + ((n >> 3) << 7);
-        s = __builtin_amdgcn_raw_buffer_load_b128(r, pinned(src_lane) + off, 0, 0);
-    }
-    __device__ __forceinline__ void store(const Stage& s, LDS_AS uint8_t* tile, int wave, int k) const {
-        u32x4 h;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // bf16 -> fp32 is a shift; fp32 -> fp16 rounds to nearest even,
-            // exact for values inside the fp16 range
-            const float lo = __builtin_bit_cast(float, s[e] << 16);
-            const float hi = __builtin_bit_cast(float, s[e] & 0xFFFF0000u);
-            h[e] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
-        }
-        // the piece's tokens are 8(n & 7) + (i >> 3); for odd n bit 3 of the
-        // token is set, which flips the low slot bit of the swizzle
-        const int n = piece(wave, k);
-        *(LDS_AS u32x4*)(tile + n * 1024 + (dst_lane ^ ((n & 1) << 4))) = h;
-    }
-};
 
 // fp8 rows (D e4m3 codes, D/32 e8m0 scales, 16-byte stride).  Wave w moves
 // tokens 16w .. 16w + 15 in pieces k < 9: lane i carries token 16w + (i & 15),
@@ -351,12 +290,6 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
 // ---------------------------------------------------------------------------
 template <bool kFp8>
 struct PiecesOf;
-template <>
-struct PiecesOf<false> {
-    typedef Bf16Pieces type;
-    static constexpr int kRowBytes = kBf16RowBytes;
-    __device__ __forceinline__ static Bf16Pieces make(int lane, int) { return Bf16Pieces(lane); }
-};
 template <>
 struct PiecesOf<true> {
     typedef Fp8Pieces type;

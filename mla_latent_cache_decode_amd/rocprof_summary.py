@@ -19,7 +19,7 @@ Usage:
   python -m mla_latent_cache_decode_amd.rocprof_summary stats --csv DIR/run_kernel_stats.csv \\
       --command "..." --out profiles/x.txt
   python -m mla_latent_cache_decode_amd.rocprof_summary traffic --fetch F.csv --write W.csv \\
-      --kernel mla_decode_kernel --copy-mb 1024 --command-fetch "..." --command-write "..." --out profiles/y.txt
+      --kernel mla_decode_bf16_kernel --copy-mb 1024 --command-fetch "..." --command-write "..." --out profiles/y.txt
 """
 
 from __future__ import annotations
@@ -32,12 +32,21 @@ import statistics
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("csrc/decode.hip", "csrc/mla_internal.h")
+# the source files each decode kernel is built from
+KERNEL_SOURCES = {
+    "mla_decode_bf16_kernel": ("csrc/decode_bf16.hip", "csrc/decode_common.h", "csrc/mla_internal.h"),
+    "mla_decode_kernel": ("csrc/decode.hip", "csrc/decode_common.h", "csrc/mla_internal.h"),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_for_dtype(kv_dtype: str) -> str:
+    """Name of the decode kernel that serves a cache dtype."""
+    return "mla_decode_bf16_kernel" if kv_dtype == "bf16" else "mla_decode_kernel"
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(PKG, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -108,7 +117,7 @@ def _traffic(args) -> str:
             sys.exit(f"no copy kernel in {path}")
         _, copy_kib = max(copies)                       # the big calibration copy
         factor = copy_bytes / (copy_kib * 1024.0)
-        mine = [v for k, vs in pk.items() if args.kernel in k for _, v in vs]
+        mine = [v for k, vs in pk.items() if _short(k).split("<")[0].split("::")[-1] == args.kernel for _, v in vs]
         if not mine:
             sys.exit(f"no {args.kernel} dispatch in {path}")
         kib = statistics.mean(mine)
@@ -118,7 +127,7 @@ def _traffic(args) -> str:
     lines = [
         f"kernel: {args.kernel}",
         f"workload: {args.workload}",
-        f"source_hash: {kernel_source_hash()}",
+        f"source_hash: {kernel_source_hash(args.kernel)}",
         f"read_bytes_per_launch: {rb}",
         f"write_bytes_per_launch: {wb}",
         f"hbm_bytes_per_launch: {rb + wb}",
