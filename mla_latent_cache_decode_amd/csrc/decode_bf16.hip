@@ -25,23 +25,23 @@
 //    accumulation).  The 64 tokens are two 32-token blocks computed one
 //    after the other, so the softmax of the first block runs on the VALU
 //    while the matrix core works on the second.
-//  * Online softmax per 32-token block, lazily rescaled: a row's running max
-//    m is raised only when a block's max exceeds it by more than 15 (log2
-//    units), and then by a multiple of 16, so the rescale of O is an exact
-//    power of two and the weights p = 2^(s - m) stay <= 2^15.  p is rounded
-//    to fp16 (its rounding is 8x finer than bf16's).
+//  * Online softmax per 32-token block with a lazy running max m: a row's
+//    first block sets m, and the weights p = 2^(s - m) are rounded to fp16
+//    (8x finer than bf16).  O is never rescaled in registers: a block whose
+//    max exceeds m by more than 15 (log2 units; its weights would leave the
+//    fp16 range) marks the segment, which is then computed once more with m
+//    fixed at the first pass's final value.
 //  * P.V is split by output dims: wave w accumulates O^T for dims
 //    128w .. 128w + 127 of all 128 rows (4 x 4 blocks of 32 x 32, 256
 //    AGPRs).  Each wave publishes its rows' P^T fragments in LDS; the V^T
 //    fragments come from the tile through transposed reads
 //    (ds_read_b64_tr_b16) and are converted bf16 -> fp16 in registers, so
 //    every cache element is read from LDS once per P.V and converted once.
-//    A block's rescale of row r travels with r's first P^T fragment of the
-//    block: the exponent step (7 bits) sits in the sign bits of the eight
-//    weights, which are otherwise zero.
 //  * Three workgroup barriers per tile: after the first block's weights are
 //    published, after the second's, and at the end (page p + 1 landed,
 //    tile p and the weights no longer read).
+//  * Epilogue: the normalised rows are staged row-major in the idle tile
+//    LDS and written as whole rows (fp16 for a split's partial).
 #include "decode_common.h"
 
 namespace mla {

@@ -28,6 +28,7 @@ import argparse
 import csv
 import hashlib
 import os
+import re
 import statistics
 import sys
 
@@ -44,11 +45,20 @@ def kernel_for_dtype(kv_dtype: str) -> str:
     return "mla_decode_bf16_kernel" if kv_dtype == "bf16" else "mla_decode_kernel"
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines (comment edits do not
+    change the kernel; a string literal holding // is not expected here)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", l).rstrip() for l in text.splitlines()]
+    return "\n".join(l for l in lines if l.strip())
+
+
 def kernel_source_hash(kernel: str) -> str:
+    """Hash of the code (comments stripped) a decode kernel is built from."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(PKG, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(PKG, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
