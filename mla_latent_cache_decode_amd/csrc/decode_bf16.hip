@@ -159,11 +159,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             make_rsrc((const uint8_t*)(a.block_table + (int64_t)b * a.max_blocks), p_hi * 4);
         auto load_phys = [&](int p) -> int { return __builtin_amdgcn_raw_buffer_load_b32(bt, p * 4, 0, 0); };
         // descriptor of logical page p (physical page phys); size 0 past p_hi
-        auto page_rsrc = [&](int p, int phys) {
-            const int nv = p < p_hi ? min(max(n_load - p * kPage, 0), kPage) : 0;
-            return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes,
-                             nv * kBf16RowBytes);
+        // rows of logical page p the workgroup loads (0 past p_hi); uniform
+        auto page_rows = [&](int p) {
+            return __builtin_amdgcn_readfirstlane(p < p_hi ? min(max(n_load - p * kPage, 0), kPage) : 0);
         };
+        auto rsrc_of = [&](int phys, int rows) {
+            return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes,
+                             rows * kBf16RowBytes);
+        };
+        auto page_rsrc = [&](int p, int phys) { return rsrc_of(phys, page_rows(p)); };
         // piece k of this wave: 1 KiB = 8 rows of one 64-dim column block
         auto dma_piece = [&](__amdgpu_buffer_rsrc_t r, LDS_AS uint8_t* tile, int k) {
             const int pn = wave * kDmaPerWave + k;
@@ -176,13 +180,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
         rs.m = -__builtin_inff();
         // a second pass runs only if a block overflowed the first pass's m
         for (int pass = 0;; ++pass) {
+        // segment prologue: the first block-table entries, the queries while
+        // they are in flight (loads complete in order, so waiting for the
+        // entry does not wait for the queries), then the first page
         const int phys0 = load_phys(p_lo);
         int phys_next = load_phys(p_lo + 1);
-        {
-            const __amdgpu_buffer_rsrc_t r0 = page_rsrc(p_lo, phys0);
-#pragma unroll
-            for (int k = 0; k < kDmaPerWave; ++k) dma_piece(r0, tiles[0], k);
-        }
+        int rows0 = page_rows(p_lo);
+        // held in an SGPR from here: a VGPR copy would be spilled across the
+        // query loads, and its reload would wait for all of them
+        asm volatile("" : "+s"(rows0));
         // this wave's 32 query rows as bf16 B-operands: lane i holds row
         // i & 31, elements 8 (i >> 5) .. + 7 of each 16-element k-step.
         // Loaded per pass (from L2 on a second pass) so that they are not
@@ -193,6 +199,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             const uint16_t* qrow = a.q + ((int64_t)b * M + row) * kD + (lane0 >> 5) * 8;
 #pragma unroll
             for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8*)(qrow + ks * 16);
+        }
+        {
+            const __amdgpu_buffer_rsrc_t r0 = rsrc_of(phys0, rows0);
+#pragma unroll
+            for (int k = 0; k < kDmaPerWave; ++k) dma_piece(r0, tiles[0], k);
         }
         rs.l = 0.f;
         bool overflow = false;
