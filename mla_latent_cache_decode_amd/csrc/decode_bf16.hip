@@ -61,8 +61,11 @@ static_assert(4 * kDmaPerWave * 1024 == kTileBytes, "four waves move a page");
 // at LDS address dst + 16 i.  Issued as asm: the compiler cannot tell that it
 // does not alias the tile being read and would otherwise wait for it
 // (vmcnt(0)) before every LDS read.  Completion is waited for explicitly.
+// The cache is streamed once per workgroup: non-temporal (nt) loads keep it
+// from displacing other data in the caches (measured -3.5 % on the long
+// context workload).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, uint32_t dst) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(dst) : "memory");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r), "{m0}"(dst) : "memory");
 }
 
 // bf16 pair -> fp16 pair (round to nearest even; exact inside the fp16 range)
