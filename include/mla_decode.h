@@ -139,8 +139,9 @@ mla_status_t mla_decode_run(mla_decode_handle_t h,
                             void* hip_stream);
 
 /* mla_decode_set_profile_events -- measurement hook.  When both are non-NULL,
- * later runs record ev_start immediately before and ev_stop immediately after
- * the split-KV decode kernel (not the planner or combine) on the run's stream.
+ * later runs have ev_start and ev_stop take the start and end timestamps of
+ * the split-KV decode kernel's own dispatch (not the combine) on the run's
+ * stream, so their elapsed time is that kernel's duration.
  * Both are hipEvent_t passed as void*, owned by the caller.  NULL, NULL turns
  * the hook off.  Not thread-safe with concurrent runs on the same handle. */
 mla_status_t mla_decode_set_profile_events(mla_decode_handle_t h, void* ev_start, void* ev_stop);

@@ -194,6 +194,7 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     plan.seq_nsplit = (int32_t*)(ws + l.seq_nsplit);
     plan.seq_slot = (int32_t*)(ws + l.seq_slot);
     plan.part_lse = (float*)(ws + l.part_lse);
+    plan.slots = h->partial_slots;
     plan.part_o = (uint16_t*)(ws + l.part_o);
     hipStream_t stream = (hipStream_t)hip_stream;
 
@@ -215,11 +216,12 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     da.overhead_units = kOverheadUnits;
     da.min_quota = kMinQuota;
     da.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
-    if (h->ev_start && hipEventRecord(h->ev_start, stream) != hipSuccess) return MLA_ERR_HIP;
-    const hipError_t e = h->p.kv_dtype == MLA_KV_BF16 ? mla::launch_decode_bf16(da, h->row_groups, stream)
-                                                      : mla::launch_decode_fp8(da, h->row_groups, stream);
+    // profile events (both or neither) take the decode kernel's own timestamps
+    const hipEvent_t e0 = h->ev_start && h->ev_stop ? h->ev_start : nullptr;
+    const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
+    const hipError_t e = h->p.kv_dtype == MLA_KV_BF16 ? mla::launch_decode_bf16(da, h->row_groups, stream, e0, e1)
+                                                      : mla::launch_decode_fp8(da, h->row_groups, stream, e0, e1);
     if (e != hipSuccess) return MLA_ERR_HIP;
-    if (h->ev_stop && hipEventRecord(h->ev_stop, stream) != hipSuccess) return MLA_ERR_HIP;
 
     mla::CombineArgs ca;
     ca.plan = plan;

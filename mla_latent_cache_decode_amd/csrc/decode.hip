@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
                 if (slot < 0) {
                     if (a.lse) a.lse[(int64_t)b * M + row] = lse_v;
                 } else {
-                    a.plan.part_lse[(int64_t)slot * M + row] = lse_v;
+                    a.plan.part_lse[(int64_t)row * a.plan.slots + slot] = lse_v;
                 }
             }
         }
@@ -537,9 +537,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
 
 }  // namespace
 
-hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream) {
-    hipLaunchKernelGGL(mla_decode_kernel<true>, dim3(a.num_workers * row_groups), dim3(kDecodeThreads), 0,
-                       stream, a);
+hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                             hipEvent_t ev_stop) {
+    hipExtLaunchKernelGGL(mla_decode_kernel<true>, dim3(a.num_workers * row_groups), dim3(kDecodeThreads), 0,
+                          stream, ev_start, ev_stop, 0, a);
     return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // translation units.  Not installed; the public ABI is include/mla_decode.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -30,8 +31,9 @@ constexpr int kMaxSplits = kMaxWorkers;       // a sequence has at most one spli
 struct PlanView {
     int32_t* seq_nsplit;        // [batch]
     int32_t* seq_slot;          // [batch]
-    float* part_lse;            // [slots][M]
+    float* part_lse;            // [M][slots]: one row's split LSEs are contiguous
     uint16_t* part_o;           // fp16 [slots][M][kDc]: a split's O / l
+    int32_t slots;              // partial slot capacity (row stride of part_lse)
 };
 
 struct DecodeArgs {
@@ -62,8 +64,13 @@ struct CombineArgs {
 };
 
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
-hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t stream);
-hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream);
+// ev_start / ev_stop (may be null): events that take the decode kernel's own
+// start and end timestamps (recorded with its dispatch, not as separate
+// stream packets).
+hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                              hipEvent_t ev_stop);
+hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                             hipEvent_t ev_stop);
 // max_splits: an upper bound on the splits of one sequence (the worker
 // count); it sizes the combine's LDS and picks its shape.
 hipError_t launch_combine(const CombineArgs& a, int max_splits, hipStream_t stream);

@@ -3,9 +3,10 @@
 // The log-sum-exp merge of a sequence's partial results,
 //     lse = log sum_i exp(lse_i),   out = sum_i exp(lse_i - lse) * out_i,
 // which is exact because each partial out_i is already normalised by its own
-// softmax denominator (the partials are stored as fp16, the sums are fp32).  The decode kernel records, per sequence, how many
-// splits it produced and where its partial slots start; a sequence served
-// by a single worker was finished by the decode kernel and is skipped here.
+// softmax denominator (the partials are stored as fp16, the sums are fp32).
+// The decode kernel records, per sequence, how many splits it produced and
+// where its partial slots start; a sequence served by a single worker was
+// finished by the decode kernel and is skipped here.
 #include "mla_internal.h"
 
 namespace mla {
@@ -13,19 +14,22 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Two shapes of the same merge, chosen by the expected split count:
-//  * many splits per sequence (few, long sequences): one row per block,
-//    the row's splits dealt to WPR waves in contiguous ranges, partial sums
-//    reduced through LDS;
-//  * few splits per sequence: a wave merges 4 rows at once, splits in
-//    chunks of 64 merged online.
-// Either way a lane owns 8 dims (one 16-byte fp16 load per split and row)
-// and many split loads are in flight together, so the merge is bound by HBM
-// rate rather than by load latency.
-constexpr int kMergeRows = 4;
-constexpr int kLoadBatch = 16;      // split loads in flight per wave, one row
-constexpr int kRowBatch = 2;        // splits per row per batch, 4 rows
+// One kernel shape, two instantiations chosen by the expected split count.
+// A block merges RPB rows; each row's splits are dealt to WPR waves in
+// contiguous ranges (WPR = 8, RPB = 1 for few long sequences with many
+// splits; WPR = 1, RPB = 4 when sequences have few splits).  A lane owns 8
+// dims of the row: one 16-byte fp16 load per split.
+//
+// Latency is the cost to beat: the whole merge is one round of loads.  Each
+// wave issues the row's split LSEs and its first kLoadBatch partial rows
+// together, and forms the max and the sum while the partial rows are still
+// in flight.  Loads go through buffer descriptors that end at the wave's
+// last split, so a batch never branches around its loads (branches would
+// make the compiler wait for every load at the join) and the lanes of a
+// short batch read zeros without touching memory.
+constexpr int kLoadBatch = 16;      // partial rows in flight per wave
 
 __device__ __forceinline__ float wave_max(float v) {
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -35,10 +39,29 @@ __device__ __forceinline__ float wave_sum(float v) {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
     return v;
 }
+
+// Buffer descriptor over [base, base + bytes); both wave-uniform.  Loads at
+// or past `bytes` return zeros and read nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, int i) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0));
+}
+__device__ __forceinline__ f16x8 load_row8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __device__ __forceinline__ void acc_add(f32x4 (&acc)[2], float w, const f16x8& h) {
     acc[0] += w * f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
     acc[1] += w * f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
 }
+
 __device__ __forceinline__ void store_row(const CombineArgs& a, int b, int row, int t, const f32x4 (&acc)[2],
                                           float mx, float sum) {
     float* o = a.out + ((int64_t)b * a.rows + row) * kDc + t * 8;
@@ -49,154 +72,114 @@ __device__ __forceinline__ void store_row(const CombineArgs& a, int b, int row, 
     if (a.lse && t == 0) a.lse[(int64_t)b * a.rows + row] = dead ? -__builtin_inff() : mx + logf(sum);
 }
 
-template <int WPR>
-__global__ __launch_bounds__(WPR * 64) void combine_split_parallel(CombineArgs a) {
-    // LDS: partial sums of waves 1.. [WPR - 1][2][64], reductions [2][WPR],
-    // then the split weights [splits]
-    extern __shared__ f32x4 s_acc[];
-    float* const s_red = (float*)(s_acc + (WPR - 1) * 2 * 64);
-    float* const s_w = s_red + 2 * WPR;
-    const int M = a.rows;
-    const int b = blockIdx.x / M, row = blockIdx.x % M;
+template <int WPR, int RPB>
+__global__ __launch_bounds__(WPR * RPB * 64) void combine_kernel(CombineArgs a) {
+    // partial sums of waves 1 .. WPR - 1 of each row, reduced by its wave 0
+    __shared__ f32x4 s_acc[WPR > 1 ? RPB * (WPR - 1) * 2 * 64 : 1];
+    const int M = a.rows;                                 // a multiple of 32, so of RPB
     const int tid = threadIdx.x, wave = tid >> 6, t = tid & 63;
-    const int n = a.plan.seq_nsplit[b];
+    const int rw = wave / WPR, part = wave % WPR;
+    const int rblocks = M / RPB;
+    const int b = blockIdx.x / rblocks;
+    const int row = (blockIdx.x % rblocks) * RPB + rw;
+    const int n = max(a.plan.seq_nsplit[b], 0);
     if (n == 1) return;                                   // finished by the decode kernel
-    const int base = a.plan.seq_slot[b];
-    float mx = -__builtin_inff();
-    for (int i = tid; i < n; i += WPR * 64) {
-        const float v = a.plan.part_lse[(int64_t)(base + i) * M + row];
-        s_w[i] = v;
-        mx = fmaxf(mx, v);
-    }
-    mx = wave_max(mx);
-    if (t == 0) s_red[wave] = mx;
-    __syncthreads();
-    mx = s_red[0];
-#pragma unroll
-    for (int q = 1; q < WPR; ++q) mx = fmaxf(mx, s_red[q]);
-    float sum = 0.f;
-    for (int i = tid; i < n; i += WPR * 64) {
-        const float e = mx == -__builtin_inff() ? 0.f : expf(s_w[i] - mx);
-        s_w[i] = e;
-        sum += e;
-    }
-    sum = wave_sum(sum);
-    if (t == 0) s_red[WPR + wave] = sum;
-    __syncthreads();                                      // weights and sums visible
-    sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < WPR; ++q) sum += s_red[WPR + q];
-    const int per = (max(n, 0) + WPR - 1) / WPR;
-    const int lo = min(wave * per, max(n, 0)), hi = min(lo + per, max(n, 0));
-    const int64_t stride = (int64_t)M * kDc;
-    const uint16_t* src = a.plan.part_o + ((int64_t)base * M + row) * kDc + t * 8;
+    const float ninf = -__builtin_inff();
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (n == 0) {                                         // an empty sequence: nothing visible
+        if (part == 0) store_row(a, b, row, t, acc, ninf, 0.f);
+        return;
+    }
+    const int base = a.plan.seq_slot[b];
+    const int per = (n + WPR - 1) / WPR;
+    const int lo = min(part * per, n), hi = min(lo + per, n);
+    const uint32_t stride = (uint32_t)M * kDc * 2;        // bytes between split slots of a row
+    const float* const lse_row = a.plan.part_lse + (int64_t)row * a.plan.slots + base;
+    const __amdgpu_buffer_rsrc_t r_lse = make_rsrc(lse_row, (uint32_t)n * 4);
+    const __amdgpu_buffer_rsrc_t r_own = make_rsrc(lse_row + lo, (uint32_t)(hi - lo) * 4);
+    // partial rows of this wave's splits j .. j + kLoadBatch - 1 (one
+    // descriptor per batch keeps every offset far inside 32 bits)
+    auto batch_rsrc = [&](int j) {
+        return make_rsrc(a.plan.part_o + ((int64_t)(base + lo + j) * M + row) * kDc,
+                         (uint32_t)max(min(kLoadBatch, hi - lo - j), 0) * stride);
+    };
+
+    // the round of loads: LSEs first, then the partial rows
+    float l_a = load_f32(r_lse, t);
+    float l_b = load_f32(r_lse, 64 + t);
+    float l_own = load_f32(r_own, t);
+    f16x8 v[kLoadBatch];
+    {
+        const __amdgpu_buffer_rsrc_t r_o = batch_rsrc(0);
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u) v[u] = load_row8(r_o, u * stride + t * 16);
+    }
+    l_a = t < n ? l_a : ninf;
+    l_b = 64 + t < n ? l_b : ninf;
+    l_own = t < hi - lo ? l_own : ninf;
+
+    // max and sum over every split of the row (each wave forms them itself)
+    float mx = fmaxf(l_a, l_b);
+    for (int c = 128; c < n; c += 64) mx = fmaxf(mx, c + t < n ? load_f32(r_lse, c + t) : ninf);
+    mx = wave_max(mx);
+    const bool dead = mx == ninf;                         // no visible token in any split
+    float sum = dead ? 0.f : expf(l_a - mx) + expf(l_b - mx);
+    for (int c = 128; c < n && !dead; c += 64) sum += c + t < n ? expf(load_f32(r_lse, c + t) - mx) : 0.f;
+    sum = wave_sum(sum);
+
+    // this wave's splits, 64 weights at a time (lane u holds split c + u's)
 #pragma unroll 1
-    for (int i = lo; i < hi; i += kLoadBatch) {
-        f16x8 v[kLoadBatch];
-        // bounds are wave-uniform: the tail batch issues only its loads
+    for (int c = 0; c < hi - lo; c += 64) {
+        if (c > 0) {
+            const float l = load_f32(r_own, c + t);
+            l_own = c + t < hi - lo ? l : ninf;
+        }
+        const float w = dead ? 0.f : expf(l_own - mx);
+        const int cn = min(64, hi - lo - c);
+#pragma unroll 1
+        for (int i = 0; i < cn; i += kLoadBatch) {
+            if (c > 0 || i > 0) {                         // the first batch is already loaded
+                const __amdgpu_buffer_rsrc_t r_o = batch_rsrc(c + i);
 #pragma unroll
-        for (int u = 0; u < kLoadBatch; ++u)
-            if (i + u < hi) v[u] = *(const f16x8*)(src + (i + u) * stride);
+                for (int u = 0; u < kLoadBatch; ++u) v[u] = load_row8(r_o, u * stride + t * 16);
+            }
 #pragma unroll
-        for (int u = 0; u < kLoadBatch; ++u)
-            if (i + u < hi) acc_add(acc, s_w[i + u], v[u]);
+            for (int u = 0; u < kLoadBatch; ++u) {
+                // past the wave's range the load gave zeros; its lane index
+                // may still be a real split of the next chunk, so mask it
+                const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), i + u));
+                acc_add(acc, i + u < cn ? wu : 0.f, v[u]);
+            }
+        }
     }
-    if (wave > 0) {
-        s_acc[((wave - 1) * 2 + 0) * 64 + t] = acc[0];
-        s_acc[((wave - 1) * 2 + 1) * 64 + t] = acc[1];
-    }
-    __syncthreads();
-    if (wave == 0) {
+    if constexpr (WPR > 1) {
+        if (part > 0) {
+            s_acc[((rw * (WPR - 1) + part - 1) * 2 + 0) * 64 + t] = acc[0];
+            s_acc[((rw * (WPR - 1) + part - 1) * 2 + 1) * 64 + t] = acc[1];
+        }
+        __syncthreads();
+        if (part > 0) return;
 #pragma unroll
         for (int q = 0; q < WPR - 1; ++q) {
-            acc[0] += s_acc[(q * 2 + 0) * 64 + t];
-            acc[1] += s_acc[(q * 2 + 1) * 64 + t];
-        }
-        store_row(a, b, row, t, acc, mx, sum);
-    }
-}
-
-__global__ __launch_bounds__(256) void combine_row_parallel(CombineArgs a) {
-    const int M = a.rows;
-    const int rblocks = (M + 4 * kMergeRows - 1) / (4 * kMergeRows);
-    const int b = blockIdx.x / rblocks;
-    const int wave = threadIdx.x >> 6, t = threadIdx.x & 63;
-    const int row0 = (blockIdx.x % rblocks) * 4 * kMergeRows + wave * kMergeRows;
-    if (row0 >= M) return;
-    const int n = a.plan.seq_nsplit[b];
-    if (n == 1) return;                                   // finished by the decode kernel
-    const int nr = min(kMergeRows, M - row0);           // rows of this wave
-    const int base = a.plan.seq_slot[b];
-    const int64_t stride = (int64_t)M * kDc;              // between split slots
-    const uint16_t* const src0 = a.plan.part_o + ((int64_t)base * M + row0) * kDc + t * 8;
-    const float ninf = -__builtin_inff();
-    float mx[kMergeRows], sum[kMergeRows];
-    f32x4 acc[kMergeRows][2];
-#pragma unroll
-    for (int j = 0; j < kMergeRows; ++j) {
-        mx[j] = ninf;
-        sum[j] = 0.f;
-        acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll 1
-    for (int c = 0; c < n; c += 64) {
-        const int cn = min(64, n - c);
-        // this chunk's LSEs (lane = split), then weights against the new max
-        float w[kMergeRows];
-#pragma unroll
-        for (int j = 0; j < kMergeRows; ++j)
-            w[j] = (t < cn && j < nr) ? a.plan.part_lse[(int64_t)(base + c + t) * M + row0 + j] : ninf;
-#pragma unroll
-        for (int j = 0; j < kMergeRows; ++j) {
-            const float m_new = fmaxf(mx[j], wave_max(w[j]));
-            // rows with nothing visible so far keep weight 0
-            const float scale = m_new == ninf ? 0.f : expf(mx[j] - m_new);
-            w[j] = m_new == ninf ? 0.f : expf(w[j] - m_new);
-            sum[j] = sum[j] * scale + wave_sum(w[j]);
-            acc[j][0] *= scale;
-            acc[j][1] *= scale;
-            mx[j] = m_new;
-        }
-#pragma unroll 1
-        for (int i = 0; i < cn; i += kRowBatch) {
-            constexpr int kU = kRowBatch;
-            f16x8 v[kMergeRows][kU];
-            // bounds are wave-uniform: the tail batch issues only its loads
-#pragma unroll
-            for (int u = 0; u < kU; ++u)
-#pragma unroll
-                for (int j = 0; j < kMergeRows; ++j)
-                    if (i + u < cn && j < nr) v[j][u] = *(const f16x8*)(src0 + (c + i + u) * stride + j * kDc);
-#pragma unroll
-            for (int u = 0; u < kU; ++u)
-#pragma unroll
-                for (int j = 0; j < kMergeRows; ++j)
-                    if (i + u < cn && j < nr) {
-                        // the weight of split c + i + u sits in lane i + u
-                        const float wu =
-                            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w[j]), i + u));
-                        acc_add(acc[j], wu, v[j][u]);
-                    }
+            acc[0] += s_acc[((rw * (WPR - 1) + q) * 2 + 0) * 64 + t];
+            acc[1] += s_acc[((rw * (WPR - 1) + q) * 2 + 1) * 64 + t];
         }
     }
-#pragma unroll
-    for (int j = 0; j < kMergeRows; ++j)
-        if (j < nr) store_row(a, b, row0 + j, t, acc[j], mx[j], sum[j]);
+    store_row(a, b, row, t, acc, mx, sum);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int max_splits, hipStream_t stream) {
     if ((int64_t)a.batch * a.rows == 0) return hipSuccess;
+    if (a.rows % 32 != 0) return hipErrorInvalidValue;
     // expected splits per sequence: the workers spread over the batch
     const int per_seq = max_splits / max(a.batch, 1);
     if (per_seq >= 32) {
-        const size_t lds = (size_t)(max_splits + 2 * 8) * sizeof(float) + 7 * 2 * 64 * 16;
-        hipLaunchKernelGGL(combine_split_parallel<8>, dim3((unsigned)(a.batch * a.rows)), dim3(512), lds, stream, a);
+        hipLaunchKernelGGL((combine_kernel<8, 1>), dim3((unsigned)(a.batch * a.rows)), dim3(512), 0, stream, a);
     } else {
-        const int rblocks = (a.rows + 4 * kMergeRows - 1) / (4 * kMergeRows);
-        hipLaunchKernelGGL(combine_row_parallel, dim3((unsigned)(a.batch * rblocks)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((combine_kernel<1, 4>), dim3((unsigned)(a.batch * (a.rows / 4))), dim3(256), 0, stream,
+                           a);
     }
     return hipGetLastError();
 }
