@@ -72,7 +72,10 @@ typedef struct mla_decode_params {
     int32_t n_h;                /* heads, a multiple of 32, <= 1024                         */
     int32_t d_c;                /* latent width; this build: 512                            */
     int32_t d_r;                /* RoPE key width; this build: 64                           */
-    int32_t block_size;         /* tokens per page; this build: 64                          */
+    int32_t block_size;         /* tokens per page block: a power of two, 16..256 (64 is the
+                                   usual size, 32 that of a ratio-2 compressed layer:
+                                   "DeepSeek-R1" record, engine kernel constraint (1));
+                                   other sizes give MLA_ERR_UNSUPPORTED                    */
     int32_t max_blocks_per_seq; /* row stride (in entries) of block_table, >= 1             */
     int32_t kv_dtype;           /* an mla_kv_dtype_t                                        */
     float   softmax_scale;      /* multiplies q.row; finite and > 0 (e.g. 1/sqrt(192))      */

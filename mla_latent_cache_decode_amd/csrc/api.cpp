@@ -70,7 +70,8 @@ mla_status_t validate_params(const mla_decode_params_t* p) {
     if ((p->d_c + p->d_r) % 32 != 0 && p->kv_dtype == MLA_KV_FP8_E4M3_E8M0) return MLA_ERR_INVALID_ARGUMENT;
     // valid requests outside what this build instantiates
     if (p->d_c != mla::kDc || p->d_r != mla::kDr) return MLA_ERR_UNSUPPORTED;
-    if (p->block_size != mla::kPage) return MLA_ERR_UNSUPPORTED;
+    if (p->block_size < 16 || p->block_size > 256 || (p->block_size & (p->block_size - 1)) != 0)
+        return MLA_ERR_UNSUPPORTED;
     return MLA_OK;
 }
 
@@ -208,6 +209,7 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     da.plan = plan;
     da.page_bytes = (int64_t)h->p.block_size *
                     (int64_t)mla_kv_row_stride(h->p.kv_dtype, h->p.d_c, h->p.d_r);
+    da.page_size = h->p.block_size;
     da.batch = batch;
     da.s_q = h->p.s_q;
     da.n_h = h->p.n_h;

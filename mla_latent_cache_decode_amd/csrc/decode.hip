@@ -86,12 +86,13 @@ struct Fp8Pieces {
         uint32_t scale;
     };
 
-    int src_lane;       // token * 608 + 16 * (i >> 4)
+    int src_lane;       // (token - tok0) * 608 + 16 * (i >> 4), inside the wave's page
     int dst_lane;       // tile_off(token, 2 * (i >> 4)) without the column block
 
-    __device__ __forceinline__ Fp8Pieces(int lane, int wave) {
+    // tok0: the tile token at which the wave's page descriptor starts
+    __device__ __forceinline__ Fp8Pieces(int lane, int wave, int tok0) {
         const int t = wave * 16 + (lane & 15);
-        src_lane = t * kFp8RowBytes + ((lane >> 4) << 4);
+        src_lane = (t - tok0) * kFp8RowBytes + ((lane >> 4) << 4);
         dst_lane = tile_off(t, 2 * (lane >> 4));
     }
     __device__ __forceinline__ void issue(Stage& s, __amdgpu_buffer_rsrc_t r, int, int k) const {
@@ -288,20 +289,13 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
 // ---------------------------------------------------------------------------
 // the decode kernel
 // ---------------------------------------------------------------------------
-template <bool kFp8>
-struct PiecesOf;
-template <>
-struct PiecesOf<true> {
-    typedef Fp8Pieces type;
-    static constexpr int kRowBytes = kFp8RowBytes;
-    __device__ __forceinline__ static Fp8Pieces make(int lane, int wave) { return Fp8Pieces(lane, wave); }
-};
-
-template <bool kFp8>
+template <int PS>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArgs a) {
-    typedef typename PiecesOf<kFp8>::type Pieces;
+    typedef Fp8Pieces Pieces;
+    typedef PageGeom<PS> Geom;
     constexpr int kPieces = Pieces::kPieces;
-    constexpr int kRowBytes = PiecesOf<kFp8>::kRowBytes;
+    constexpr int kRowBytes = kFp8RowBytes;
+    static_assert(Geom::kRangeTok % 16 == 0, "a wave's 16 tokens lie in one page");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
@@ -324,6 +318,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
     const int64_t w_lo = (int64_t)worker * Q, w_hi = w_lo + Q;
 
     LDS_AS uint8_t* const tiles[2] = {lds, lds + kTileBytes};
+    // first token (within a tile) of the page this wave loads from
+    const int tok0 = Geom::tok0(wave);
     // this wave's q_R fragments, lane-major: fragment f of lane l at f*1024 + l*16
     LDS_AS uint8_t* const qr_lds = lds + kLdsTiles + wave * (kQLdsSteps * 1024) + (tid & 63) * 16;
 
@@ -352,13 +348,22 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         // page loads on vmcnt; a scalar load would share lgkmcnt with the
         // LDS traffic and make every LDS wait a full drain).  Entries of
         // pages at or past p_hi read 0 and are not used.
-        const __amdgpu_buffer_rsrc_t bt =
-            make_rsrc((const uint8_t*)(a.block_table + (int64_t)b * a.max_blocks), p_hi * 4);
-        auto load_phys = [&](int p) -> int { return __builtin_amdgcn_raw_buffer_load_b32(bt, p * 4, 0, 0); };
-        // descriptor of logical page p (physical page phys); size 0 past p_hi
+        // The entry read for tile p is that of the page holding token tok0
+        // of the tile (the wave's page); an entry past the sequence's last
+        // page may be read but is not used (its rows are past n_load).
+        const __amdgpu_buffer_rsrc_t bt = make_rsrc((const uint8_t*)(a.block_table + (int64_t)b * a.max_blocks),
+                                                    (PS < kPage ? min(Geom::entries(p_hi), a.max_blocks)
+                                                                : Geom::entries(p_hi)) * 4);
+        auto load_phys = [&](int p) -> int {
+            return __builtin_amdgcn_raw_buffer_load_b32(bt, Geom::entry(p, tok0) * 4, 0, 0);
+        };
+        // descriptor over the rows of tile p in the wave's page (physical
+        // page phys) that the workgroup loads; size 0 past p_hi
         auto page_rsrc = [&](int p, int phys) {
-            const int nv = p < p_hi ? min(max(n_load - p * kPage, 0), kPage) : 0;
-            return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes, nv * kRowBytes);
+            const int nv = p < p_hi ? min(max(n_load - p * kPage - tok0, 0), Geom::kRangeTok) : 0;
+            return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes +
+                                 Geom::row_in_page(p, tok0) * kRowBytes,
+                             nv * kRowBytes);
         };
 
         // this wave's 32 query rows as MFMA B operands (q_abs || q_R): bf16
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
                 *(LDS_AS f16x8*)(qr_lds + (ks - kQRegSteps) * 1024) = qf[ks];
         };
         const f16x8(&qreg)[kQRegSteps] = *reinterpret_cast<const f16x8(*)[kQRegSteps]>(&qf[0]);
-        const Pieces pc = PiecesOf<kFp8>::make(opaque_lane(), wave);
+        const Pieces pc(opaque_lane(), wave, tok0);
 
         // ---- Page pipeline, one barrier per tile.  Pieces stream through
         // VGPRs (converted or dequantised in registers) into the idle
@@ -539,8 +544,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                              hipEvent_t ev_stop) {
-    hipExtLaunchKernelGGL(mla_decode_kernel<true>, dim3(a.num_workers * row_groups), dim3(kDecodeThreads), 0,
-                          stream, ev_start, ev_stop, 0, a);
+    const dim3 grid(a.num_workers * row_groups), block(kDecodeThreads);
+    switch (a.page_size) {
+        case 16: hipExtLaunchKernelGGL(mla_decode_kernel<16>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 32: hipExtLaunchKernelGGL(mla_decode_kernel<32>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 64: hipExtLaunchKernelGGL(mla_decode_kernel<64>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 128: hipExtLaunchKernelGGL(mla_decode_kernel<128>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 256: hipExtLaunchKernelGGL(mla_decode_kernel<256>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -105,7 +105,9 @@ __device__ __forceinline__ bool raise_max(float mx, RowState& rs) {
     return need && !fresh;
 }
 
+template <int PS>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
+    typedef PageGeom<PS> Geom;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBf16];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
     int* sbuf = (int*)smem;                 // planner scratch; dead before the first page lands
@@ -130,6 +132,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
     LDS_AS uint8_t* const tiles[2] = {lds, lds + kTileBytes};
     LDS_AS uint8_t* const pbuf = lds + 2 * kTileBytes;
     const int lane0 = tid & 63;
+    // first token (within a tile) of the page this wave loads from
+    const int tok0 = Geom::tok0(wave);
     // direct-to-LDS source offset of this lane inside a page piece: token
     // i >> 3 of the piece, the chunk whose swizzled slot is i & 7 (pieces
     // of odd row blocks flip the slot's low bit: address ^ 16)
@@ -156,26 +160,45 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
         const int n_vis = active ? L - a.s_q + 1 + j_wave : 0;     // tokens this wave's rows see
         const int n_load = L - a.s_q + 1 + j_last;                  // tokens the workgroup loads
 
-        // block-table entries by vector loads, a tile ahead of their use;
-        // entries at or past p_hi read 0 and are not used
-        const __amdgpu_buffer_rsrc_t bt =
-            make_rsrc((const uint8_t*)(a.block_table + (int64_t)b * a.max_blocks), p_hi * 4);
-        auto load_phys = [&](int p) -> int { return __builtin_amdgcn_raw_buffer_load_b32(bt, p * 4, 0, 0); };
-        // descriptor of logical page p (physical page phys); size 0 past p_hi
-        // rows of logical page p the workgroup loads (0 past p_hi); uniform
-        auto page_rows = [&](int p) {
-            return __builtin_amdgcn_readfirstlane(p < p_hi ? min(max(n_load - p * kPage, 0), kPage) : 0);
+        // block-table entries by vector loads, a tile ahead of their use:
+        // the entry of the page holding token tok0 of tile p.  Entries the
+        // segment cannot touch read 0; an entry past the sequence's last
+        // page is read but not used (its rows are past n_load)
+        const __amdgpu_buffer_rsrc_t bt = make_rsrc((const uint8_t*)(a.block_table + (int64_t)b * a.max_blocks),
+                                                    (PS < kPage ? min(Geom::entries(p_hi), a.max_blocks)
+                                                                : Geom::entries(p_hi)) * 4);
+        auto load_phys = [&](int p) -> int {
+            return __builtin_amdgcn_raw_buffer_load_b32(bt, Geom::entry(p, tok0) * 4, 0, 0);
         };
-        auto rsrc_of = [&](int phys, int rows) {
-            return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes,
+        // rows of tile p this wave's page holds for the workgroup (0 past p_hi); uniform
+        auto page_rows = [&](int p) {
+            return __builtin_amdgcn_readfirstlane(
+                p < p_hi ? min(max(n_load - p * kPage - tok0, 0), Geom::kRangeTok) : 0);
+        };
+        // descriptor over those rows of physical page phys
+        auto rsrc_of = [&](int p, int phys, int rows) {
+            return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes +
+                                 Geom::row_in_page(p, tok0) * kBf16RowBytes,
                              rows * kBf16RowBytes);
         };
-        auto page_rsrc = [&](int p, int phys) { return rsrc_of(phys, page_rows(p)); };
-        // piece k of this wave: 1 KiB = 8 rows of one 64-dim column block
+        auto page_rsrc = [&](int p, int phys) { return rsrc_of(p, phys, page_rows(p)); };
+        // piece k of this wave: 1 KiB = 8 rows (token group g) of one 64-dim
+        // column block cb, from the wave's page; it lands at LDS piece
+        // cb * 8 + g of the tile.  g and k agree in their low bit (the
+        // swizzle's slot flip).
         auto dma_piece = [&](__amdgpu_buffer_rsrc_t r, LDS_AS uint8_t* tile, int k) {
-            const int pn = wave * kDmaPerWave + k;
-            const int off = (pn & 7) * 8 * kBf16RowBytes + ((pn >> 3) << 7);
-            dma16(r, (pinned(dma_lane) ^ ((k & 1) << 4)) + off, (uint32_t)(uintptr_t)(tile + pn * 1024));
+            if constexpr (Geom::kRanges == 1) {
+                const int pn = wave * kDmaPerWave + k;
+                const int off = (pn & 7) * 8 * kBf16RowBytes + ((pn >> 3) << 7);
+                dma16(r, (pinned(dma_lane) ^ ((k & 1) << 4)) + off, (uint32_t)(uintptr_t)(tile + pn * 1024));
+            } else {
+                constexpr int kGroups = 8 / Geom::kRanges;        // token groups of 8 in one page
+                const int i = (wave % Geom::kWavesPerRange) * kDmaPerWave + k;
+                const int gl = i % kGroups, cb = i / kGroups;
+                const int pn = cb * 8 + tok0 / 8 + gl;
+                const int off = gl * 8 * kBf16RowBytes + (cb << 7);
+                dma16(r, (pinned(dma_lane) ^ ((k & 1) << 4)) + off, (uint32_t)(uintptr_t)(tile + pn * 1024));
+            }
         };
 
         const float scale_log2 = a.scale_log2;
@@ -204,7 +227,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8*)(qrow + ks * 16);
         }
         {
-            const __amdgpu_buffer_rsrc_t r0 = rsrc_of(phys0, rows0);
+            const __amdgpu_buffer_rsrc_t r0 = rsrc_of(p_lo, phys0, rows0);
 #pragma unroll
             for (int k = 0; k < kDmaPerWave; ++k) dma_piece(r0, tiles[0], k);
         }
@@ -557,8 +580,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                               hipEvent_t ev_stop) {
-    hipExtLaunchKernelGGL(mla_decode_bf16_kernel, dim3(a.num_workers * row_groups), dim3(kDecodeThreads), 0, stream,
-                          ev_start, ev_stop, 0, a);
+    const dim3 grid(a.num_workers * row_groups), block(kDecodeThreads);
+    switch (a.page_size) {
+        case 16: hipExtLaunchKernelGGL(mla_decode_bf16_kernel<16>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 32: hipExtLaunchKernelGGL(mla_decode_bf16_kernel<32>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 64: hipExtLaunchKernelGGL(mla_decode_bf16_kernel<64>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 128: hipExtLaunchKernelGGL(mla_decode_bf16_kernel<128>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 256: hipExtLaunchKernelGGL(mla_decode_bf16_kernel<256>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

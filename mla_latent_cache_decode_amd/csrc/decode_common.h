@@ -249,6 +249,40 @@ __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_i
     return ws;
 }
 
+// Page blocks of PS tokens (a power of two, 16 .. 256) under 64-token tiles
+// ("DeepSeek-R1" record, engine kernel constraint (1): decode kernels are
+// instantiated per page-block size; 64 is the common one, 32 the block of a
+// ratio-2 compressed layer).  When PS < 64 a tile spans kRanges pages, one
+// per run of kRangeTok consecutive tokens, and each wave loads from one of
+// them only (kWavesPerRange waves per page), so a wave still needs a single
+// block-table entry and a single buffer descriptor per tile.  When PS >= 64
+// a tile lies inside one page, at row (p * 64) % PS.
+template <int PS>
+struct PageGeom {
+    static_assert(PS >= 16 && PS <= 256 && (PS & (PS - 1)) == 0, "page block: a power of two in 16 .. 256");
+    static constexpr int kRanges = PS < kPage ? kPage / PS : 1;
+    static constexpr int kRangeTok = kPage / kRanges;
+    static constexpr int kWavesPerRange = (kDecodeThreads / 64) / kRanges;
+    static_assert(kWavesPerRange >= 1, "every page of a tile needs a wave");
+    // first token (within a tile) of the pages wave w loads from
+    __device__ static constexpr int tok0(int wave) { return kRanges == 1 ? 0 : (wave / kWavesPerRange) * kRangeTok; }
+    // block-table entry, and row inside that page, of token tok0 of tile p
+    // (written per case so that the page-block size of 64 compiles to plain p)
+    __device__ static constexpr int entry(int p, int t0) {
+        if constexpr (PS < kPage) return p * kRanges + t0 / PS;
+        else return p / (PS / kPage);
+    }
+    __device__ static constexpr int row_in_page(int p, int t0) {
+        if constexpr (PS <= kPage) return 0;
+        else return (p % (PS / kPage)) * kPage;
+    }
+    // block-table entries a segment ending at tile p_hi may touch
+    __device__ static constexpr int entries(int p_hi) {
+        if constexpr (PS < kPage) return p_hi * kRanges;
+        else return (p_hi + PS / kPage - 1) / (PS / kPage);
+    }
+};
+
 // Buffer descriptor over [base, base + bytes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int bytes) {
     // both inputs are wave-uniform; say so, or the compiler wraps each load

@@ -9,8 +9,10 @@
 
 namespace mla {
 
-// Shapes this build instantiates (guide section 1.1: 512 latent + 64 RoPE;
-// "DeepSeek-R1" record, constraint (1): page block of 64 tokens).
+// Shapes this build instantiates (guide section 1.1: 512 latent + 64 RoPE).
+// The decode works on tiles of 64 tokens whatever the page-block size
+// ("DeepSeek-R1" record, constraint (1): decode kernels are instantiated per
+// page-block size; 64 is the usual one, 32 that of a compressed layer).
 constexpr int kPage = 64;
 constexpr int kDc = 512;
 constexpr int kDr = 64;
@@ -45,6 +47,7 @@ struct DecodeArgs {
     float* lse;                 // [B][M] or null
     PlanView plan;
     int64_t page_bytes;         // bytes per page
+    int32_t page_size;          // tokens per page block (16 .. 256, a power of two)
     int32_t batch;
     int32_t s_q;
     int32_t n_h;

@@ -90,7 +90,9 @@ def _init(**over):
     (dict(num_workers=-1), 1),
     (dict(flags=4), 1),
     (dict(d_c=448), 2),          # valid request, not instantiated in this build
-    (dict(block_size=32), 2),
+    (dict(block_size=48), 2),    # page blocks: powers of two from 16 to 256
+    (dict(block_size=8), 2),
+    (dict(block_size=512), 2),
 ])
 def test_init_rejects_before_any_hip_call(over, expected):
     st, h = _init(**over)
@@ -113,11 +115,12 @@ def test_init_null_arguments():
     assert lib.mla_decode_init(ctypes.byref(p), None) == 1
 
 
-def test_valid_params_without_a_gpu_report_hip_error():
+@pytest.mark.parametrize("block_size", [16, 32, 64, 128, 256])
+def test_valid_params_without_a_gpu_report_hip_error(block_size):
     import torch
     if torch.cuda.is_available():
         pytest.skip("this host has a GPU")
-    st, h = _init()
+    st, h = _init(block_size=block_size)
     assert st == 4 and h is None
 
 

@@ -83,6 +83,66 @@ def test_paged_equals_identity_bitwise(name):
     np.testing.assert_array_equal(l1, l2)
 
 
+def _repage(w, page: int, seed: int):
+    """The same logical cache laid out in page blocks of `page` tokens: each
+    sequence's rows copied in order into a seeded permutation of physical
+    blocks, with NaN-poisoned tails and spare blocks.  The decode works on
+    64-token tiles whatever the block size, so its output must not change by
+    a single bit."""
+    s = w.spec
+    rng = np.random.default_rng(seed)
+    lens = w.seq_lens.astype(np.int64)
+    nb = (lens + page - 1) // page
+    n_used = int(nb.sum())
+    pool_pages = n_used + 3
+    phys = rng.permutation(pool_pages)[:n_used]
+    pool = np.empty((pool_pages, page) + w.pool.shape[2:], dtype=w.pool.dtype)
+    if s.kv_dtype == "bf16":
+        pool[...] = 0x7FC0
+    else:
+        pool[...] = 0xFF
+        pool[..., :s.d] = 0x7F
+    bt = np.full((s.batch, max(int(nb.max()), 1)), -1, dtype=np.int32)
+    off = 0
+    for b in range(s.batch):
+        n64 = (int(lens[b]) + 63) // 64
+        rows = w.pool[w.block_table[b, :n64]].reshape((n64 * 64,) + w.pool.shape[2:])[:lens[b]]
+        for k in range(int(nb[b])):
+            seg = rows[k * page:(k + 1) * page]
+            pool[phys[off + k], :len(seg)] = seg
+            bt[b, k] = phys[off + k]
+        off += int(nb[b])
+    spec = dataclasses.replace(s, page=page, name=f"{s.name}_p{page}")
+    return dataclasses.replace(w, spec=spec, pool=pool, block_table=bt)
+
+
+@pytest.mark.parametrize("name", ["paged_b32_small", "fp8_b64_small", "mtp2_b128_small", "long_ctx_b4_small"])
+@pytest.mark.parametrize("page", [16, 32, 128, 256])
+def test_page_block_sizes(name, page):
+    # page blocks other than 64 ("DeepSeek-R1" record, constraint (1): 32 for
+    # a compressed layer): bitwise the 64-token result, and the oracle's
+    # result through its own gather at that block size
+    w64 = make_workload(name)
+    w = _repage(w64, page, seed=page)
+    o64, l64 = run_gpu(w64, num_workers=7)
+    o, l = run_gpu(w, num_workers=7)
+    np.testing.assert_array_equal(o, o64)
+    np.testing.assert_array_equal(l, l64)
+    ro, rl = oracle(w)
+    assert_parity(w, o, l, ro, rl)
+
+
+@pytest.mark.parametrize("name,page", [("paged_b32", 32), ("fp8_b64", 128)])
+def test_page_block_sizes_full_size_sampled(name, page):
+    # a full-size workload generated at another block size, default plan
+    w = make_workload(dataclasses.replace(SPECS[name], page=page, name=f"{name}_p{page}"))
+    batches = sorted({0, w.spec.batch // 2, int(np.argmax(w.seq_lens))})
+    out, lse = run_gpu(w)
+    ro, rl = oracle(w, batches=batches)
+    assert_parity(w, out, lse, ro, rl, batches=batches)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
 @pytest.mark.parametrize("name", ["long_ctx_b4_small", "fp8_b64_small"])
 def test_repeat_runs_bitwise_identical(name):
     w = make_workload(name)
