@@ -15,6 +15,12 @@ Draw order (torch CPU generator, seeded per workload):
      (for FP8 first an outlier mask per chunk, then the values), then
      rounded to bf16 (round-to-nearest-even) or quantised to FP8
   4. queries: float32 N(0,1) times the workload's q scale, rounded to bf16
+  5. sparse workloads only ("DeepSeek-V3.2" record: a top-k selector,
+     index_topk = 2048, picks the tokens each query attends over): for every
+     (sequence, query position) in order, a random permutation of its
+     visible tokens 0 .. L - s_q + j, cut to topk entries, or padded with -1
+     when the context is shorter than topk.  The selection is uniform: the
+     indexer's scores are not modelled, only its output format.
 
 Poisoning (never read by a correct decode): tail slots after the last token
 of each sequence, every spare page, and FP8 row padding.  bf16 poison is the
@@ -52,6 +58,7 @@ class WorkloadSpec:
     outlier_p: float = 0.0
     outlier_mult: float = 1.0
     spare_pages: int = 64
+    topk: int = 0                   # > 0: sparse decode over topk selected tokens per query
     seed: int = 0
     softmax_scale: float = 1.0 / math.sqrt(192.0)
 
@@ -68,12 +75,23 @@ class Workload:
     block_table: np.ndarray     # int32 [B, max_blocks]
     seq_lens: np.ndarray        # int32 [B]
     row_stride: int             # bytes per cached row
+    indices: Optional[np.ndarray] = None   # sparse: int32 [B, s_q, topk] token positions, -1 = padding
+
+    @property
+    def selected_tokens(self) -> int:
+        """Cache rows the decode reads: every visible token of every sequence
+        (dense), or the valid entries of every query's index list (sparse)."""
+        if self.indices is None:
+            return int(self.seq_lens.astype(np.int64).sum())
+        s_q = self.spec.s_q
+        n_vis = (self.seq_lens.astype(np.int64)[:, None] - s_q + 1 + np.arange(s_q)[None, :])[:, :, None]
+        return int(((self.indices >= 0) & (self.indices < n_vis)).sum())
 
     @property
     def kv_bytes_algorithmic(self) -> int:
-        """Bytes of cache payload the decode must read: sum_b L_b x row payload."""
+        """Bytes of cache payload the decode must read: rows read x row payload."""
         per_row = 2 * self.spec.d if self.spec.kv_dtype == "bf16" else self.spec.d + self.spec.d // 32
-        return int(self.seq_lens.astype(np.int64).sum()) * per_row
+        return self.selected_tokens * per_row
 
 
 def fp8_row_stride(d: int) -> int:
@@ -96,6 +114,10 @@ SPECS = {
                             outlier_p=0.01, outlier_mult=20.0, seed=4),
     # two queries per sequence (MTP-style), causal over the last two positions
     "mtp2_b128": WorkloadSpec("mtp2_b128", 128, ("loguniform", 512, 32768), s_q=2, seed=5),
+    # sparse top-k decode ("DeepSeek-V3.2" record: index_topk 2048) over contexts
+    # longer than topk, bf16 paged cache
+    "sparse_topk2048_b64": WorkloadSpec("sparse_topk2048_b64", 64, ("uniform", 4096, 32768), topk=2048,
+                                        seed=6),
 }
 
 # reduced-size variants of the same recipes for element-by-element parity
@@ -110,6 +132,10 @@ SPECS.update({
                                          seq_lens=("uniform", 100, 2100), spare_pages=8),
     "mtp2_b128_small": dataclasses.replace(SPECS["mtp2_b128"], name="mtp2_b128_small", batch=6,
                                            seq_lens=("loguniform", 40, 1500), spare_pages=8),
+    # contexts both shorter (index lists padded with -1) and longer than topk
+    "sparse_topk2048_b64_small": dataclasses.replace(SPECS["sparse_topk2048_b64"], name="sparse_topk2048_b64_small",
+                                                     batch=5, seq_lens=("uniform", 100, 3000), topk=700,
+                                                     spare_pages=8),
 })
 
 # the long-context workload is the one the bandwidth target is stated on
@@ -222,17 +248,30 @@ def make_workload(spec: Union[str, WorkloadSpec], seed: Optional[int] = None) ->
     qf = torch.randn((spec.batch, spec.s_q, spec.n_h, d), generator=gen) * spec.q_scale
     q_bits = qf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
+    # 5. sparse index lists
+    indices = None
+    if spec.topk > 0:
+        indices = np.full((spec.batch, spec.s_q, spec.topk), -1, dtype=np.int32)
+        for b in range(spec.batch):
+            for j in range(spec.s_q):
+                n_vis = max(int(seq_lens[b]) - spec.s_q + 1 + j, 0)
+                sel = torch.randperm(n_vis, generator=gen)[:spec.topk].numpy()
+                indices[b, j, :sel.size] = sel
+
     return Workload(spec=spec, q_bits=q_bits, pool=pool, block_table=block_table,
-                    seq_lens=seq_lens, row_stride=row_stride)
+                    seq_lens=seq_lens, row_stride=row_stride, indices=indices)
 
 
 def to_torch(w: Workload, device) -> dict:
     """Device tensors for the decode call (plain copies of the same bytes)."""
     q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(device)
     pool_bytes = torch.from_numpy(np.ascontiguousarray(w.pool).view(np.uint8)).to(device)
-    return {
+    d = {
         "q": q.contiguous(),
         "kv": pool_bytes.contiguous(),
         "block_table": torch.from_numpy(w.block_table).to(device).contiguous(),
         "seq_lens": torch.from_numpy(w.seq_lens).to(device).contiguous(),
     }
+    if w.indices is not None:
+        d["indices"] = torch.from_numpy(w.indices).to(device).contiguous()
+    return d

@@ -16,11 +16,14 @@ Every floating-point step runs in float64.  Sources, by page:
   (FP8 latent row: e4m3 codes over every dimension, RoPE dimensions included,
   plus one e8m0 scale per 32 codes).
 * Same guide, section 4: E4M3 max normal 448.
+* "DeepSeek-V3.2" model record: the same latent cache, read through a
+  top-k selector (index_topk = 2048) -- the sparse decode.
 
 Modules
 -------
 formats     bf16 / e4m3fn / e8m0 decoding and cache-row decoding
 mla         the absorbed MLA decode definition (scores, softmax, latent output)
+sparse      the same decode over each query's selected tokens only (top-k)
 unabsorbed  the explicit per-head MHA form (up-projected keys and values)
 brute       pure-Python triple loop for tiny inputs
 footprint   closed-form cache sizes
@@ -30,5 +33,6 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 force); none is "parity unpinned".
 """
 
-from . import formats, mla, unabsorbed, brute, footprint  # noqa: F401
+from . import formats, mla, sparse, unabsorbed, brute, footprint  # noqa: F401
 from .mla import mla_decode_ref  # noqa: F401
+from .sparse import mla_sparse_decode_ref  # noqa: F401

@@ -73,3 +73,39 @@ def mla_decode_brute(q_bits, pool, block_table, seq_lens, *, kv_dtype: str, d_c:
                     out[b][j][h][i] = acc / z
                 lse[b][j][h] = m + math.log(z)
     return np.array(out, dtype=np.float64), np.array(lse, dtype=np.float64)
+
+
+def mla_sparse_decode_brute(q_bits, pool, block_table, seq_lens, indices, *, kv_dtype: str, d_c: int,
+                            d_r: int, page: int, softmax_scale: float):
+    """The sparse (top-k) decode one scalar at a time: query j of sequence b
+    attends to the listed tokens t with 0 <= t < L - s_q + 1 + j only."""
+    B, s_q, n_h, d = np.asarray(q_bits).shape
+    out = [[[[0.0] * d_c for _ in range(n_h)] for _ in range(s_q)] for _ in range(B)]
+    lse = [[[0.0] * n_h for _ in range(s_q)] for _ in range(B)]
+    for b in range(B):
+        L = int(seq_lens[b])
+        for j in range(s_q):
+            n_vis = max(L - s_q + 1 + j, 0)
+            toks = [int(t) for t in indices[b][j] if 0 <= int(t) < n_vis]
+            rows = [_row_values(pool, int(block_table[b][t // page]), t % page, kv_dtype, d) for t in toks]
+            for h in range(n_h):
+                q = [_bf16(x) for x in q_bits[b][j][h]]
+                if not rows:
+                    lse[b][j][h] = -math.inf
+                    continue
+                scores = []
+                for row in rows:
+                    acc = 0.0
+                    for i in range(d):
+                        acc += q[i] * row[i]
+                    scores.append(softmax_scale * acc)
+                m = max(scores)
+                w = [math.exp(s - m) for s in scores]
+                z = sum(w)
+                for i in range(d_c):
+                    acc = 0.0
+                    for t in range(len(rows)):
+                        acc += w[t] * rows[t][i]
+                    out[b][j][h][i] = acc / z
+                lse[b][j][h] = m + math.log(z)
+    return np.array(out, dtype=np.float64), np.array(lse, dtype=np.float64)
