@@ -6,7 +6,9 @@ work plan, then the LSE combine) over one batch of the long-context
 workload: batch 4, seq_lens
 {32768, 65536, 131072, 131072}, n_h 128, d_c 512, d_R 64, bf16 paged cache
 (block 64, permuted pages).  Inputs are seeded synthetic data already
-resident in HBM before the timed region.
+resident in HBM before the timed region.  ``--workload`` picks another
+recipe (a parity workload, or the sparse top-k one, whose step is the
+row-table pre-pass, the gathering decode and the combine).
 
 Prints one JSON line: KV-read GB/s (whole job), TFLOP/s, the dominant
 kernel's roofline (decode kernel: algorithmic KV bytes per launch over its
@@ -53,7 +55,10 @@ def parse():
 
 
 def flops_per_step(w) -> int:
+    """2176 flop per (query row, token it attends to)."""
     s = w.spec
+    if w.indices is not None:
+        return w.selected_tokens * s.n_h * FLOP_PER_ROW_TOKEN
     tot = 0
     for L in w.seq_lens.tolist():
         for j in range(s.s_q):
@@ -66,7 +71,8 @@ def cpu_baseline(w, budget_s: float) -> dict:
     batch order, wrapping around to repeat the batch, until the time budget is
     used (always at least one sequence).  Rate = KV bytes of the sequences
     processed over the wall time."""
-    from oracle import mla_decode_ref
+    import numpy as np
+    from oracle import mla_decode_ref, mla_sparse_decode_ref
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
@@ -78,17 +84,26 @@ def cpu_baseline(w, budget_s: float) -> dict:
     t0 = time.perf_counter()
     while True:
         b = n_seq % s.batch
-        mla_decode_ref(w.q_bits, w.pool, w.block_table, w.seq_lens, kv_dtype=s.kv_dtype, d_c=s.d_c,
-                       d_r=s.d_r, page=s.page, softmax_scale=s.softmax_scale, batches=[b])
+        if w.indices is None:
+            mla_decode_ref(w.q_bits, w.pool, w.block_table, w.seq_lens, kv_dtype=s.kv_dtype, d_c=s.d_c,
+                           d_r=s.d_r, page=s.page, softmax_scale=s.softmax_scale, batches=[b])
+            n_tok = int(w.seq_lens[b])
+        else:
+            mla_sparse_decode_ref(w.q_bits, w.pool, w.block_table, w.seq_lens, w.indices, kv_dtype=s.kv_dtype,
+                                  d_c=s.d_c, d_r=s.d_r, page=s.page, softmax_scale=s.softmax_scale, batches=[b])
+            L = int(w.seq_lens[b])
+            n_vis = L - s.s_q + 1 + np.arange(s.s_q)[:, None]
+            n_tok = int(((w.indices[b] >= 0) & (w.indices[b] < n_vis)).sum())
         n_seq += 1
-        tokens += int(w.seq_lens[b])
-        nbytes += int(w.seq_lens[b]) * row_bytes
+        tokens += n_tok
+        nbytes += n_tok * row_bytes
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    what = "tokens" if w.indices is None else f"selected tokens of top-{s.topk} lists"
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n_seq} sequences of {s.name} taken in batch order, repeating the batch "
-                      f"({n_seq / s.batch:.2f} passes; {tokens} tokens, all {s.n_h} heads, s_q={s.s_q}), "
+                      f"({n_seq / s.batch:.2f} passes; {tokens} {what}, all {s.n_h} heads, s_q={s.s_q}), "
                       f"float64 numpy oracle, {dt:.2f} s wall"}
 
 
@@ -123,19 +138,27 @@ def main():
     dec = mla.MlaDecode(max_batch=s.batch, s_q=s.s_q, n_h=s.n_h, d_c=s.d_c, d_r=s.d_r, block_size=s.page,
                         max_blocks_per_seq=w.block_table.shape[1], kv_dtype=s.kv_dtype,
                         softmax_scale=s.softmax_scale, num_workers=args.num_workers)
-    ws = dec.alloc_workspace(s.batch, device=dev)
+    sparse = w.indices is not None
+    ws = dec.alloc_sparse_workspace(s.batch, s.topk, device=dev) if sparse else dec.alloc_workspace(s.batch, device=dev)
     out = torch.empty((s.batch, s.s_q, s.n_h, s.d_c), dtype=torch.float32, device=dev)
     lse = torch.empty((s.batch, s.s_q, s.n_h), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     lib = mla.load_library()
-    call = (dec._h, t["q"].data_ptr(), t["kv"].data_ptr(), t["block_table"].data_ptr(),
-            t["seq_lens"].data_ptr(), s.batch, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(),
-            stream.cuda_stream)
+    if sparse:
+        entry = lib.mla_decode_sparse_run
+        call = (dec._h, t["q"].data_ptr(), t["kv"].data_ptr(), t["block_table"].data_ptr(),
+                t["seq_lens"].data_ptr(), t["indices"].data_ptr(), s.topk, s.batch, out.data_ptr(),
+                lse.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
+    else:
+        entry = lib.mla_decode_run
+        call = (dec._h, t["q"].data_ptr(), t["kv"].data_ptr(), t["block_table"].data_ptr(),
+                t["seq_lens"].data_ptr(), s.batch, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(),
+                stream.cuda_stream)
 
     def step():
-        st = lib.mla_decode_run(*call)
+        st = entry(*call)
         if st != 0:
-            raise mla.MlaError(st, "mla_decode_run")
+            raise mla.MlaError(st, entry.__name__)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -204,6 +227,7 @@ def main():
                    "d_r": s.d_r, "page": s.page, "kv_dtype": s.kv_dtype,
                    "seq_lens": w.seq_lens.tolist() if s.batch <= 8 else f"{s.seq_lens}",
                    "total_tokens": int(w.seq_lens.sum()), "kv_bytes": kv_bytes,
+                   **({"topk": s.topk, "selected_tokens": w.selected_tokens} if sparse else {}),
                    "workers": info["num_workers"], "row_groups": info["row_groups"],
                    "compute_units": info["compute_units"]},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),

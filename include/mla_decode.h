@@ -141,6 +141,52 @@ mla_status_t mla_decode_run(mla_decode_handle_t h,
                             size_t workspace_bytes,
                             void* hip_stream);
 
+/* mla_decode_sparse_workspace_size -- device workspace bytes that
+ * mla_decode_sparse_run needs for `batch` sequences (0 <= batch <= max_batch)
+ * and index lists of `topk` entries (1 <= topk <= 2^20).  `bytes` is a host
+ * pointer.  Besides the work plan and split partials of batch * s_q query
+ * units, the workspace holds the gather table of the pre-pass: one 4-byte
+ * row id per index entry (rounded up to 64 per unit) and one 8-byte mask per
+ * 64 entries (and a 2 KiB row of zeros that entries which do not take
+ * part are fetched from). */
+mla_status_t mla_decode_sparse_workspace_size(mla_decode_handle_t h, int32_t batch, int32_t topk,
+                                              size_t* bytes);
+
+/* mla_decode_sparse_run -- one sparse (top-k) decode step: the "DeepSeek-V3.2"
+ * model record keeps the latent cache of the dense decode but has a top-k
+ * selector (index_topk = 2048) choose, for every query token, the tokens it
+ * attends over.  Query j of sequence b computes the dense decode's result
+ * over the tokens listed in indices[b][j] only.
+ *   indices     : device, int32 [batch][s_q][topk], 4-byte aligned: logical
+ *                 token positions of sequence b.  An entry takes part iff
+ *                 0 <= t < L_b - s_q + 1 + j (the query's causal context);
+ *                 padding such as -1, and any other value, is ignored.
+ *                 Entries count as listed: a selector returns distinct
+ *                 positions (a repeated one would count twice).  A query
+ *                 with no valid entry gets out = 0 and lse = -inf.
+ *   topk        : entries per list, 1 .. 2^20.
+ *   every other argument as for mla_decode_run (the handle's s_q, n_h,
+ *   block_size and softmax scale apply); workspace >=
+ *   mla_decode_sparse_workspace_size(batch, topk) bytes.
+ * The handle must be for a bf16 cache (fp8: MLA_ERR_UNSUPPORTED).  Enqueues
+ * three kernels on the stream: the pre-pass that turns index lists into
+ * physical row ids (through the block table) and masks, the decode that
+ * gathers those rows, and the split combine.  Only the listed rows are read;
+ * the block-table entries of listed valid tokens must be valid pages. */
+mla_status_t mla_decode_sparse_run(mla_decode_handle_t h,
+                                   const void* q,
+                                   const void* kv_pages,
+                                   const int32_t* block_table,
+                                   const int32_t* seq_lens,
+                                   const int32_t* indices,
+                                   int32_t topk,
+                                   int32_t batch,
+                                   float* out,
+                                   float* lse,
+                                   void* workspace,
+                                   size_t workspace_bytes,
+                                   void* hip_stream);
+
 /* mla_decode_set_profile_events -- measurement hook.  When both are non-NULL,
  * later runs have ev_start and ev_stop take the start and end timestamps of
  * the split-KV decode kernel's own dispatch (not the combine) on the run's

@@ -32,6 +32,8 @@ EXPORTED_SYMBOLS = (
     "mla_decode_init",
     "mla_decode_workspace_size",
     "mla_decode_run",
+    "mla_decode_sparse_workspace_size",
+    "mla_decode_sparse_run",
     "mla_decode_set_profile_events",
     "mla_decode_get_info",
     "mla_decode_free",
@@ -88,6 +90,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mla_decode_workspace_size.restype = ctypes.c_int
     lib.mla_decode_run.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.mla_decode_run.restype = ctypes.c_int
+    lib.mla_decode_sparse_workspace_size.argtypes = [vp, i32, i32, ctypes.POINTER(sz)]
+    lib.mla_decode_sparse_workspace_size.restype = ctypes.c_int
+    lib.mla_decode_sparse_run.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.mla_decode_sparse_run.restype = ctypes.c_int
     lib.mla_decode_set_profile_events.argtypes = [vp, vp, vp]
     lib.mla_decode_set_profile_events.restype = ctypes.c_int
     lib.mla_decode_get_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -201,6 +207,54 @@ class MlaDecode:
             workspace.numel() * workspace.element_size(), stream)
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_run")
+
+    # -- the sparse (top-k) decode -------------------------------------------
+    def sparse_workspace_size(self, batch: int, topk: int) -> int:
+        n = ctypes.c_size_t()
+        st = self._lib.mla_decode_sparse_workspace_size(self._h, int(batch), int(topk), ctypes.byref(n))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_decode_sparse_workspace_size")
+        return n.value
+
+    def alloc_sparse_workspace(self, batch: int, topk: int, device="cuda"):
+        import torch
+        return torch.empty(max(self.sparse_workspace_size(batch, topk), 1), dtype=torch.uint8, device=device)
+
+    def run_sparse(self, q, kv, block_table, seq_lens, indices, out, lse=None, workspace=None,
+                   stream=None) -> None:
+        """Each query attends to the tokens its row of ``indices`` (int32
+        [batch, s_q, topk], -1 = padding) lists; see mla_decode_sparse_run."""
+        import torch
+        p = self.params
+        batch = int(seq_lens.shape[0])
+        _check(q, (batch, p.s_q, p.n_h, p.d_c + p.d_r), torch.bfloat16, "q")
+        _check(out, (batch, p.s_q, p.n_h, p.d_c), torch.float32, "out")
+        if lse is not None:
+            _check(lse, (batch, p.s_q, p.n_h), torch.float32, "lse")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != batch \
+                or block_table.shape[1] != p.max_blocks_per_seq or not block_table.is_contiguous():
+            raise ValueError("block_table must be contiguous int32 [batch, max_blocks_per_seq]")
+        if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens must be contiguous int32 [batch]")
+        if indices.dtype != torch.int32 or indices.dim() != 3 or tuple(indices.shape[:2]) != (batch, p.s_q) \
+                or not indices.is_contiguous():
+            raise ValueError("indices must be contiguous int32 [batch, s_q, topk]")
+        if not kv.is_contiguous() or not kv.is_cuda:
+            raise ValueError("kv pages must be a contiguous device tensor")
+        for t in (q, out, block_table, seq_lens, indices) + ((lse,) if lse is not None else ()):
+            if not t.is_cuda:
+                raise ValueError("all tensors must be on the GPU")
+        topk = int(indices.shape[2])
+        if workspace is None:
+            workspace = self.alloc_sparse_workspace(batch, topk, device=q.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = self._lib.mla_decode_sparse_run(
+            self._h, q.data_ptr(), kv.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), indices.data_ptr(),
+            topk, batch, out.data_ptr(), lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), stream)
+        if st != MLA_OK:
+            raise MlaError(st, "mla_decode_sparse_run")
 
     def close(self) -> None:
         if getattr(self, "_h", None):

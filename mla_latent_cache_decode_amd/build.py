@@ -5,6 +5,7 @@ Usage: python -m mla_latent_cache_decode_amd.build   (or __graft_entry__.build()
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -16,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["decode_bf16.hip", "decode.hip", "plan_combine.hip", "api.cpp"]
+SOURCES = ["decode_bf16.hip", "decode.hip", "plan_combine.hip", "sparse_rows.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -50,13 +51,18 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, extra_flags=None) -> str:
     """Compile every HIP source for gfx950 and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
     flags = COMMON_FLAGS + list(extra_flags or [])
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        _run([HIPCC] + flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        cmds.append([HIPCC] + flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # the translation units compile independently: one hipcc each, in parallel
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB_PATH + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB_PATH)

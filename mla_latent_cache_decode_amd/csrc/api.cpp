@@ -55,6 +55,78 @@ WsLayout layout(const mla_decode_handle* h, int32_t batch) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+constexpr int32_t kMaxTopk = 1 << 20;
+
+// Workspace of a sparse run: the plan and partials of batch * s_q units of
+// n_h rows, the row table and the tile masks of the pre-pass.
+struct SparseLayout {
+    size_t seq_nsplit, seq_slot, part_lse, part_o, rows, masks, zero_row, total;
+    int units, tiles, row_groups, workers, slots;
+};
+
+SparseLayout sparse_layout(const mla_decode_handle* h, int32_t batch, int32_t topk) {
+    SparseLayout l{};
+    l.units = (batch > 0 ? batch : 1) * h->p.s_q;
+    l.tiles = (topk + mla::kPage - 1) / mla::kPage;
+    l.row_groups = (h->p.n_h + mla::kRowsPerGroup - 1) / mla::kRowsPerGroup;
+    // as many workgroups as the dense decode of this handle launches
+    if (h->p.num_workers > 0) {
+        l.workers = h->p.num_workers;
+    } else {
+        int w = h->num_workers * h->row_groups / l.row_groups;
+        if (w >= 8) w = w / 8 * 8;
+        l.workers = w < 1 ? 1 : (w > mla::kMaxWorkers ? mla::kMaxWorkers : w);
+    }
+    l.slots = l.workers > 1 ? 2 * (l.workers - 1) : 1;
+    const size_t nu = (size_t)l.units;
+    size_t off = 0;
+    l.seq_nsplit = off;  off += align_up(nu * sizeof(int32_t));
+    l.seq_slot = off;    off += align_up(nu * sizeof(int32_t));
+    l.part_lse = off;    off += align_up((size_t)l.slots * h->p.n_h * sizeof(float));
+    l.part_o = off;      off += align_up((size_t)l.slots * h->p.n_h * mla::kDc * sizeof(uint16_t));
+    l.rows = off;        off += align_up(nu * l.tiles * mla::kPage * sizeof(uint32_t));
+    l.masks = off;       off += align_up(nu * l.tiles * sizeof(uint64_t));
+    l.zero_row = off;    off += align_up(mla::kSparseZeroRowBytes);
+    l.total = off;
+    return l;
+}
+
+mla_status_t check_run_pointers(const void* q, const void* kv_pages, const int32_t* block_table,
+                                const int32_t* seq_lens, const float* out, const float* lse, const void* workspace) {
+    if (!q || !kv_pages || !block_table || !seq_lens || !out || !workspace) return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(out, 16)) return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, kAlign)) return MLA_ERR_INVALID_ARGUMENT;
+    return MLA_OK;
+}
+
+// The decode arguments a dense and a sparse run share.
+mla::DecodeArgs decode_args(const mla_decode_handle* h, const void* q, const void* kv_pages,
+                            const int32_t* block_table, const int32_t* seq_lens, float* out, float* lse,
+                            const mla::PlanView& plan) {
+    mla::DecodeArgs da{};
+    da.q = (const uint16_t*)q;
+    da.kv = (const uint8_t*)kv_pages;
+    da.block_table = block_table;
+    da.seq_lens = seq_lens;
+    da.out = out;
+    da.lse = lse;
+    da.plan = plan;
+    da.page_bytes = (int64_t)h->p.block_size * (int64_t)mla_kv_row_stride(h->p.kv_dtype, h->p.d_c, h->p.d_r);
+    da.page_size = h->p.block_size;
+    da.n_h = h->p.n_h;
+    da.max_blocks = h->p.max_blocks_per_seq;
+    da.overhead_units = kOverheadUnits;
+    da.min_quota = kMinQuota;
+    da.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
+    da.sparse_topk = 0;
+    da.sparse_rows = nullptr;
+    da.sparse_masks = nullptr;
+    da.sparse_zero_row = nullptr;
+    return da;
+}
+
 mla_status_t validate_params(const mla_decode_params_t* p) {
     if (p->struct_size != (int32_t)sizeof(mla_decode_params_t)) return MLA_ERR_INVALID_ARGUMENT;
     if (p->max_batch < 1 || p->max_batch > (1 << 20)) return MLA_ERR_INVALID_ARGUMENT;
@@ -182,16 +254,13 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     if (!h) return MLA_ERR_INVALID_ARGUMENT;
     if (batch < 0 || batch > h->p.max_batch) return MLA_ERR_INVALID_ARGUMENT;
     if (batch == 0) return MLA_OK;
-    if (!q || !kv_pages || !block_table || !seq_lens || !out || !workspace) return MLA_ERR_INVALID_ARGUMENT;
-    if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(out, 16)) return MLA_ERR_INVALID_ARGUMENT;
-    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
-        return MLA_ERR_INVALID_ARGUMENT;
-    if (!aligned(workspace, kAlign)) return MLA_ERR_INVALID_ARGUMENT;
+    const mla_status_t v = check_run_pointers(q, kv_pages, block_table, seq_lens, out, lse, workspace);
+    if (v != MLA_OK) return v;
     const WsLayout l = layout(h, batch);
     if (workspace_bytes < l.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
     uint8_t* ws = (uint8_t*)workspace;
-    mla::PlanView plan;
+    mla::PlanView plan{};
     plan.seq_nsplit = (int32_t*)(ws + l.seq_nsplit);
     plan.seq_slot = (int32_t*)(ws + l.seq_slot);
     plan.part_lse = (float*)(ws + l.part_lse);
@@ -199,25 +268,10 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     plan.part_o = (uint16_t*)(ws + l.part_o);
     hipStream_t stream = (hipStream_t)hip_stream;
 
-    mla::DecodeArgs da;
-    da.q = (const uint16_t*)q;
-    da.kv = (const uint8_t*)kv_pages;
-    da.block_table = block_table;
-    da.seq_lens = seq_lens;
-    da.out = out;
-    da.lse = lse;
-    da.plan = plan;
-    da.page_bytes = (int64_t)h->p.block_size *
-                    (int64_t)mla_kv_row_stride(h->p.kv_dtype, h->p.d_c, h->p.d_r);
-    da.page_size = h->p.block_size;
+    mla::DecodeArgs da = decode_args(h, q, kv_pages, block_table, seq_lens, out, lse, plan);
     da.batch = batch;
     da.s_q = h->p.s_q;
-    da.n_h = h->p.n_h;
-    da.max_blocks = h->p.max_blocks_per_seq;
     da.num_workers = h->num_workers;
-    da.overhead_units = kOverheadUnits;
-    da.min_quota = kMinQuota;
-    da.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
     // profile events (both or neither) take the decode kernel's own timestamps
     const hipEvent_t e0 = h->ev_start && h->ev_stop ? h->ev_start : nullptr;
     const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
@@ -225,13 +279,83 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
                                                       : mla::launch_decode_fp8(da, h->row_groups, stream, e0, e1);
     if (e != hipSuccess) return MLA_ERR_HIP;
 
-    mla::CombineArgs ca;
+    mla::CombineArgs ca{};
     ca.plan = plan;
     ca.out = out;
     ca.lse = lse;
     ca.batch = batch;
     ca.rows = h->rows;
     if (mla::launch_combine(ca, h->num_workers, stream) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+mla_status_t mla_decode_sparse_workspace_size(mla_decode_handle_t h, int32_t batch, int32_t topk, size_t* bytes) {
+    if (!h || !bytes) return MLA_ERR_INVALID_ARGUMENT;
+    if (batch < 0 || batch > h->p.max_batch) return MLA_ERR_INVALID_ARGUMENT;
+    if (topk < 1 || topk > kMaxTopk) return MLA_ERR_INVALID_ARGUMENT;
+    *bytes = sparse_layout(h, batch, topk).total;
+    return MLA_OK;
+}
+
+mla_status_t mla_decode_sparse_run(mla_decode_handle_t h, const void* q, const void* kv_pages,
+                                   const int32_t* block_table, const int32_t* seq_lens, const int32_t* indices,
+                                   int32_t topk, int32_t batch, float* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream) {
+    if (!h) return MLA_ERR_INVALID_ARGUMENT;
+    if (batch < 0 || batch > h->p.max_batch) return MLA_ERR_INVALID_ARGUMENT;
+    if (topk < 1 || topk > kMaxTopk) return MLA_ERR_INVALID_ARGUMENT;
+    if (batch == 0) return MLA_OK;
+    const mla_status_t v = check_run_pointers(q, kv_pages, block_table, seq_lens, out, lse, workspace);
+    if (v != MLA_OK) return v;
+    if (!indices || !aligned(indices, 4)) return MLA_ERR_INVALID_ARGUMENT;
+    if (h->p.kv_dtype != MLA_KV_BF16) return MLA_ERR_UNSUPPORTED;
+    const SparseLayout l = sparse_layout(h, batch, topk);
+    if (workspace_bytes < l.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+    uint8_t* ws = (uint8_t*)workspace;
+    mla::PlanView plan{};
+    plan.seq_nsplit = (int32_t*)(ws + l.seq_nsplit);
+    plan.seq_slot = (int32_t*)(ws + l.seq_slot);
+    plan.part_lse = (float*)(ws + l.part_lse);
+    plan.slots = l.slots;
+    plan.part_o = (uint16_t*)(ws + l.part_o);
+    hipStream_t stream = (hipStream_t)hip_stream;
+
+    mla::SparseRowsArgs ra{};
+    ra.indices = indices;
+    ra.block_table = block_table;
+    ra.seq_lens = seq_lens;
+    ra.rows = (uint32_t*)(ws + l.rows);
+    ra.masks = (uint64_t*)(ws + l.masks);
+    ra.zero_row = ws + l.zero_row;
+    ra.units = l.units;
+    ra.s_q = h->p.s_q;
+    ra.topk = topk;
+    ra.tiles = l.tiles;
+    ra.max_blocks = h->p.max_blocks_per_seq;
+    ra.page_size = h->p.block_size;
+    if (mla::launch_sparse_rows(ra, stream) != hipSuccess) return MLA_ERR_HIP;
+
+    // every (sequence, query position) is a unit of n_h rows attending to its own tokens
+    mla::DecodeArgs da = decode_args(h, q, kv_pages, block_table, seq_lens, out, lse, plan);
+    da.batch = l.units;
+    da.s_q = 1;
+    da.num_workers = l.workers;
+    da.sparse_topk = topk;
+    da.sparse_rows = ra.rows;
+    da.sparse_masks = ra.masks;
+    da.sparse_zero_row = ra.zero_row;
+    const hipEvent_t e0 = h->ev_start && h->ev_stop ? h->ev_start : nullptr;
+    const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
+    if (mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1) != hipSuccess) return MLA_ERR_HIP;
+
+    mla::CombineArgs ca{};
+    ca.plan = plan;
+    ca.out = out;
+    ca.lse = lse;
+    ca.batch = l.units;
+    ca.rows = h->p.n_h;
+    if (mla::launch_combine(ca, l.workers, stream) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
 

@@ -68,6 +68,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, uint32
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r), "{m0}"(dst) : "memory");
 }
 
+// The same 1 KiB direct-to-LDS load with a 64-bit address per lane (the
+// sparse gather: every token row can sit anywhere in the cache).  No
+// instruction offset: it would move the LDS destination as well.
+__device__ __forceinline__ void dma16_gather(uint64_t addr, uint32_t dst) {
+    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(addr), "{m0}"(dst) : "memory");
+}
+
 // bf16 pair -> fp16 pair (round to nearest even; exact inside the fp16 range)
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t d) {
     const float lo = __builtin_bit_cast(float, d << 16);
@@ -105,9 +112,17 @@ __device__ __forceinline__ bool raise_max(float mx, RowState& rs) {
     return need && !fresh;
 }
 
-template <int PS>
+// kSparse: the top-k decode ("DeepSeek-V3.2" record).  A unit (one query
+// position of one sequence, n_h rows) attends to the topk rows its index
+// list selects; tile p holds entries 64p .. 64p + 63, gathered row by row
+// through the pre-pass's row table (wave w loads tokens 16w .. 16w + 15),
+// and the pre-pass's tile mask takes the place of the length mask.
+// Entries that do not take part are fetched from a row of zeros that the
+// pre-pass writes into the workspace (their weights are 0; zeros keep
+// 0 x V finite).
+template <int PS, bool kSparse>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
-    typedef PageGeom<PS> Geom;
+    typedef PageGeom<kSparse ? 16 : PS> Geom;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBf16];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
     int* sbuf = (int*)smem;                 // planner scratch; dead before the first page lands
@@ -142,7 +157,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
     int64_t cost = start.cost;
     int slot_base = start.slot;
     for (int b = start.b; b < a.batch; ++b) {
-        const int L = ld_const(a.seq_lens + b);
+        const int L = kSparse ? a.sparse_topk : ld_const(a.seq_lens + b);
         const int pages = L > 0 ? (L + kPage - 1) / kPage : 0;
         if (pages == 0) continue;
         const int64_t A = cost + a.overhead_units, E = A + pages;
@@ -201,6 +216,35 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             }
         };
 
+        // sparse gather: the row-id pair of this lane's two tokens (16w + x
+        // and 16w + 8 + x, x = lane >> 3 of a piece) and the tile mask, by
+        // vector loads two tiles ahead; tiles at or past p_hi read zeros and
+        // are never used
+        const int64_t tiles_u = kSparse ? (L + kPage - 1) / kPage : 0;
+        const __amdgpu_buffer_rsrc_t r_rows =
+            make_rsrc((const uint8_t*)(a.sparse_rows + (kSparse ? (int64_t)b * tiles_u * 64 : 0)), p_hi * 256);
+        const __amdgpu_buffer_rsrc_t r_mask =
+            make_rsrc((const uint8_t*)(a.sparse_masks + (kSparse ? (int64_t)b * tiles_u : 0)), p_hi * 8);
+        auto load_rows = [&](int p) -> u32x2 {
+            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 r_rows, p * 256 + (wave * 8 + (pinned(lane0) >> 3)) * 8, 0, 0));
+        };
+        auto load_mask = [&](int p) -> u32x2 {
+            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r_mask, p * 8, 0, 0));
+        };
+        // what entries that do not take part fetch: a row of zeros
+        const uint8_t* const zero_row = a.sparse_zero_row;
+        // piece k of tile p (row ids rw): token 16w + 8(k & 1) + x, column
+        // block k >> 1, landing at LDS piece (k >> 1) * 8 + 2w + (k & 1)
+        auto dma_sparse = [&](const u32x2& rw, int p, LDS_AS uint8_t* tile, auto k_c) {
+            constexpr int k = decltype(k_c)::value, gl = k & 1, cb = k >> 1;
+            const uint32_t row = rw[gl];
+            const uint8_t* base = (p < p_hi && row != kNoRow) ? a.kv + (uint64_t)row * kBf16RowBytes : zero_row;
+            const int l = pinned(lane0);
+            const int chunk = ((((l & 7) ^ sw(l >> 3)) << 4) ^ (gl << 4)) + cb * 128;
+            dma16_gather((uint64_t)(base + chunk), (uint32_t)(uintptr_t)(tile + (cb * 8 + 2 * wave + gl) * 1024));
+        };
+
         const float scale_log2 = a.scale_log2;
         RowState rs;
         rs.m = -__builtin_inff();
@@ -209,12 +253,23 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
         // segment prologue: the first block-table entries, the queries while
         // they are in flight (loads complete in order, so waiting for the
         // entry does not wait for the queries), then the first page
-        const int phys0 = load_phys(p_lo);
-        int phys_next = load_phys(p_lo + 1);
-        int rows0 = page_rows(p_lo);
-        // held in an SGPR from here: a VGPR copy would be spilled across the
-        // query loads, and its reload would wait for all of them
-        asm volatile("" : "+s"(rows0));
+        int phys0 = 0, phys_next = 0, rows0 = 0;
+        u32x2 rw0, rw_next, mk0, mk1;
+        uint32_t mk_lo = ~0u, mk_hi = ~0u;       // sparse: mask of the current tile
+        uint32_t mk_next_lo = ~0u, mk_next_hi = ~0u;
+        if constexpr (kSparse) {
+            rw0 = load_rows(p_lo);
+            mk0 = load_mask(p_lo);
+            rw_next = load_rows(p_lo + 1);
+            mk1 = load_mask(p_lo + 1);
+        } else {
+            phys0 = load_phys(p_lo);
+            phys_next = load_phys(p_lo + 1);
+            rows0 = page_rows(p_lo);
+            // held in an SGPR from here: a VGPR copy would be spilled across the
+            // query loads, and its reload would wait for all of them
+            asm volatile("" : "+s"(rows0));
+        }
         // this wave's 32 query rows as bf16 B-operands: lane i holds row
         // i & 31, elements 8 (i >> 5) .. + 7 of each 16-element k-step.
         // Loaded per pass (from L2 on a second pass) so that they are not
@@ -226,7 +281,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
 #pragma unroll
             for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8*)(qrow + ks * 16);
         }
-        {
+        if constexpr (kSparse) {
+            static_for<0, kDmaPerWave>([&](auto k) { dma_sparse(rw0, p_lo, tiles[0], k); });
+            mk_lo = __builtin_amdgcn_readfirstlane(mk0[0]);
+            mk_hi = __builtin_amdgcn_readfirstlane(mk0[1]);
+            mk_next_lo = __builtin_amdgcn_readfirstlane(mk1[0]);
+            mk_next_hi = __builtin_amdgcn_readfirstlane(mk1[1]);
+        } else {
             const __amdgpu_buffer_rsrc_t r0 = rsrc_of(p_lo, phys0, rows0);
 #pragma unroll
             for (int k = 0; k < kDmaPerWave; ++k) dma_piece(r0, tiles[0], k);
@@ -244,8 +305,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
         for (int p = p_lo; p < p_hi; ++p) {
             const LDS_AS uint8_t* tile = tiles[(p - p_lo) & 1];
             LDS_AS uint8_t* const tnext = tiles[(p - p_lo + 1) & 1];
-            const __amdgpu_buffer_rsrc_t r_next = page_rsrc(p + 1, phys_next);
-            const int phys_after = load_phys(p + 2);
+            __amdgpu_buffer_rsrc_t r_next;
+            int phys_after = 0;
+            u32x2 rw_after, mk_after;
+            if constexpr (kSparse) {
+                rw_after = load_rows(p + 2);
+                mk_after = load_mask(p + 2);
+            } else {
+                r_next = page_rsrc(p + 1, phys_next);
+                phys_after = load_phys(p + 2);
+            }
             const int n_valid = min(max(n_vis - p * kPage, 0), kPage);
 
             const int lane = opaque_lane();
@@ -315,7 +384,18 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
                 f32x16& sv = sblk[blk];
                 if constexpr (part == 0) {
                     score_ready(sv);
-                    if (n_valid < 32 * (blk + 1)) {
+                    if constexpr (kSparse) {
+                        // the lane's token c_r + 4 hi of the block takes part iff its mask bit is set
+                        const uint32_t mb = blk == 0 ? mk_lo : mk_hi;
+                        if (mb != ~0u) {
+                            const uint32_t ml = mb >> (4 * hi);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int c_r = ((r >> 2) << 3) + (r & 3);
+                                sv[r] = (ml >> c_r) & 1 ? sv[r] : -__builtin_inff();
+                            }
+                        }
+                    } else if (n_valid < 32 * (blk + 1)) {
                         const int nv_lane = n_valid - 32 * blk - 4 * hi;
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
@@ -385,7 +465,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
                 if constexpr (g + kAhead < kQkSteps) read_k(std::integral_constant<int, g + kAhead>{});
                 mfma_qk(sblk[blk], kf[g % (kAhead + 1)], qf[ks]);
                 // page p + 1: one direct-to-LDS load every fourth MFMA
-                if constexpr (g % 4 == 0 && g / 4 < kDmaPerWave) dma_piece(r_next, tnext, g / 4);
+                if constexpr (g % 4 == 0 && g / 4 < kDmaPerWave) {
+                    if constexpr (kSparse) dma_sparse(rw_next, p + 1, tnext, std::integral_constant<int, g / 4>{});
+                    else dma_piece(r_next, tnext, g / 4);
+                }
                 if constexpr (blk == 0) {
                     // V^T of token step 0
                     if constexpr (ks >= 6 && ks < 30 && (ks - 6) % 6 == 0)
@@ -446,7 +529,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
 #pragma unroll
                 for (int hb = 0; hb < 4; ++hb) asm volatile("" : "+a"(o[db][hb]));
             rs.l += lsum;
-            phys_next = phys_after;
+            if constexpr (kSparse) {
+                rw_next = rw_after;
+                mk_lo = mk_next_lo;
+                mk_hi = mk_next_hi;
+                mk_next_lo = __builtin_amdgcn_readfirstlane(mk_after[0]);
+                mk_next_hi = __builtin_amdgcn_readfirstlane(mk_after[1]);
+            } else {
+                phys_next = phys_after;
+            }
             // page p + 1 landed, tile p and the weights are no longer read
             __builtin_amdgcn_s_waitcnt(VMCNT0_IMM);
             __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
@@ -582,13 +673,21 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t s
                               hipEvent_t ev_stop) {
     const dim3 grid(a.num_workers * row_groups), block(kDecodeThreads);
     switch (a.page_size) {
-        case 16: hipExtLaunchKernelGGL(mla_decode_bf16_kernel<16>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 32: hipExtLaunchKernelGGL(mla_decode_bf16_kernel<32>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 64: hipExtLaunchKernelGGL(mla_decode_bf16_kernel<64>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 128: hipExtLaunchKernelGGL(mla_decode_bf16_kernel<128>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 256: hipExtLaunchKernelGGL(mla_decode_bf16_kernel<256>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 16: hipExtLaunchKernelGGL((mla_decode_bf16_kernel<16, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 32: hipExtLaunchKernelGGL((mla_decode_bf16_kernel<32, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 64: hipExtLaunchKernelGGL((mla_decode_bf16_kernel<64, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 128: hipExtLaunchKernelGGL((mla_decode_bf16_kernel<128, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 256: hipExtLaunchKernelGGL((mla_decode_bf16_kernel<256, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_bf16_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                                     hipEvent_t ev_stop) {
+    // the gather goes through the row table: the page-block size is the pre-pass's business
+    hipExtLaunchKernelGGL((mla_decode_bf16_kernel<64, true>), dim3(a.num_workers * row_groups), dim3(kDecodeThreads),
+                          0, stream, ev_start, ev_stop, 0, a);
     return hipGetLastError();
 }
 

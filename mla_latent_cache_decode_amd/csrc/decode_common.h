@@ -168,6 +168,11 @@ struct WorkerStart {
     int64_t quota;  // cost units per worker
 };
 
+// Length of sequence (or sparse unit) b on the work plan's token axis.
+__device__ __forceinline__ int plan_len(const DecodeArgs& a, int b) {
+    return a.sparse_topk > 0 ? a.sparse_topk : a.seq_lens[b];
+}
+
 // The worker's starting point on the cost axis.  With write_info it also
 // records, for every sequence whose cost position lies in this worker's
 // quota, the number of segments it is split into and its first partial slot
@@ -175,11 +180,11 @@ struct WorkerStart {
 __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_info, int* sbuf, int tid) {
     const int B = a.batch, G = a.num_workers, c = a.overhead_units;
     int t_cost = 0;
-    const int my_len = tid < B ? a.seq_lens[tid] : 0;      // reused by the first chunk
+    const int my_len = tid < B ? plan_len(a, tid) : 0;      // reused by the first chunk
     {
         int local = my_len > 0 ? (my_len + kPage - 1) / kPage + c : 0, zero = 0, tz;
         for (int b = tid + kDecodeThreads; b < B; b += kDecodeThreads) {
-            const int L = a.seq_lens[b];
+            const int L = plan_len(a, b);
             local += L > 0 ? (L + kPage - 1) / kPage + c : 0;
         }
         block_scan2(local, zero, t_cost, tz, sbuf, tid);
@@ -198,7 +203,7 @@ __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_i
         const int b = base + tid;
         int pages = 0;
         if (b < B) {
-            const int L = base == 0 ? my_len : a.seq_lens[b];
+            const int L = base == 0 ? my_len : plan_len(a, b);
             pages = L > 0 ? (L + kPage - 1) / kPage : 0;
         }
         // a sequence's segment count depends on its cost prefix, so two scans

@@ -129,6 +129,8 @@ def test_null_handle_paths():
     n = ctypes.c_size_t()
     assert lib.mla_decode_workspace_size(None, 1, ctypes.byref(n)) == 1
     assert lib.mla_decode_run(None, None, None, None, None, 1, None, None, None, 0, None) == 1
+    assert lib.mla_decode_sparse_workspace_size(None, 1, 2048, ctypes.byref(n)) == 1
+    assert lib.mla_decode_sparse_run(None, None, None, None, None, None, 2048, 1, None, None, None, 0, None) == 1
     assert lib.mla_decode_free(None) == 0
     assert lib.mla_decode_set_profile_events(None, None, None) == 1
     assert lib.mla_decode_get_info(None, None, None, None) == 1

@@ -1,0 +1,161 @@
+"""GPU parity of the sparse (top-k) decode ("DeepSeek-V3.2" record: a top-k
+selector, index_topk 2048, picks each query's tokens) through the C ABI,
+against the float64 sparse oracle on the same seeded bytes."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from mla_inputs import SPECS, WorkloadSpec, make_workload, to_torch
+from oracle import mla_sparse_decode_ref
+from gpu_helpers import assert_parity, make_decoder, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_sparse(w, num_workers=0, indices=None, with_lse=True, dec=None, tensors=None):
+    s = w.spec
+    dev = torch.device("cuda:0")
+    t = tensors if tensors is not None else to_torch(w, dev)
+    idx = t["indices"] if indices is None else torch.from_numpy(np.ascontiguousarray(indices)).to(dev)
+    dec = dec or make_decoder(w, num_workers)
+    say(f"sparse decode {s.name} B={s.batch} s_q={s.s_q} n_h={s.n_h} topk={idx.shape[2]} page={s.page} "
+        f"workers={dec.info()['num_workers']} seed={s.seed}")
+    out = torch.full((s.batch, s.s_q, s.n_h, s.d_c), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((s.batch, s.s_q, s.n_h), float("nan"), dtype=torch.float32, device=dev) if with_lse else None
+    dec.run_sparse(t["q"], t["kv"], t["block_table"], t["seq_lens"], idx, out, lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (lse.cpu().numpy() if with_lse else None)
+
+
+def sparse_oracle(w, indices=None, batches=None):
+    s = w.spec
+    return mla_sparse_decode_ref(w.q_bits, w.pool, w.block_table, w.seq_lens,
+                                 w.indices if indices is None else indices, kv_dtype=s.kv_dtype, d_c=s.d_c,
+                                 d_r=s.d_r, page=s.page, softmax_scale=s.softmax_scale, batches=batches)
+
+
+SMALL = SPECS["sparse_topk2048_b64_small"]
+VARIANTS = [
+    SMALL,
+    dataclasses.replace(SMALL, name="sparse_mtp2_small", s_q=2, seed=41),
+    dataclasses.replace(SMALL, name="sparse_heads64_small", n_h=64, seed=42),
+    dataclasses.replace(SMALL, name="sparse_heads256_small", n_h=256, batch=3, seed=43),
+    dataclasses.replace(SMALL, name="sparse_page32_small", page=32, seed=44),
+    dataclasses.replace(SMALL, name="sparse_topk64_small", topk=64, seed=45),
+    dataclasses.replace(SMALL, name="sparse_topk1_small", topk=1, seed=46),
+]
+
+
+@pytest.mark.parametrize("spec", VARIANTS, ids=[s.name for s in VARIANTS])
+@pytest.mark.parametrize("workers", [0, 1, 3, 300])
+def test_sparse_parity_small(spec, workers):
+    w = make_workload(spec)
+    out, lse = run_sparse(w, num_workers=workers)
+    ro, rl = sparse_oracle(w)
+    assert_parity(w, out, lse, ro, rl)
+
+
+def test_sparse_full_size_sampled():
+    w = make_workload("sparse_topk2048_b64")
+    batches = sorted({0, 31, 63, int(np.argmax(w.seq_lens))})
+    out, lse = run_sparse(w)
+    ro, rl = sparse_oracle(w, batches=batches)
+    assert_parity(w, out, lse, ro, rl, batches=batches)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_sparse_ignores_entries_outside_the_context():
+    # entries past the causal limit, past the sequence, huge and negative
+    w = make_workload(dataclasses.replace(SMALL, name="sparse_bad_entries", s_q=2, seed=47))
+    rng = np.random.default_rng(5)
+    idx = w.indices.copy()
+    for b in range(w.spec.batch):
+        L = int(w.seq_lens[b])
+        for j in range(w.spec.s_q):
+            n_vis = L - w.spec.s_q + 1 + j
+            pos = rng.choice(idx.shape[2], size=4, replace=False)
+            idx[b, j, pos] = [n_vis, L + 3, 1 << 30, -5]
+    out, lse = run_sparse(w, indices=idx, num_workers=5)
+    ro, rl = sparse_oracle(w, indices=idx)
+    assert_parity(w, out, lse, ro, rl)
+
+
+def test_sparse_reads_only_selected_rows():
+    # every row no list selects is NaN-poisoned: bitwise the same result
+    w = make_workload(dataclasses.replace(SMALL, name="sparse_poison", seed=48))
+    o1, l1 = run_sparse(w, num_workers=7)
+    used = np.zeros(w.pool.shape[:2], dtype=bool)
+    for b in range(w.spec.batch):
+        for t in w.indices[b, 0]:
+            if 0 <= t < int(w.seq_lens[b]):
+                used[w.block_table[b, t // 64], t % 64] = True
+    pool = w.pool.copy()
+    pool[~used] = 0x7FC0
+    o2, l2 = run_sparse(dataclasses.replace(w, pool=pool), num_workers=7)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_sparse_over_whole_context_equals_dense_bitwise():
+    # index lists 0 .. L-1 in order (padded with -1) visit the dense decode's
+    # tiles in the dense order; with one worker neither run splits, so the
+    # two must agree bit for bit
+    spec = WorkloadSpec("sparse_vs_dense", 3, ("fixed", (700, 64, 1500)), topk=1500, spare_pages=4, seed=49)
+    w = make_workload(spec)
+    idx = np.full_like(w.indices, -1)
+    for b in range(spec.batch):
+        idx[b, 0, :w.seq_lens[b]] = np.arange(w.seq_lens[b])
+    o_s, l_s = run_sparse(w, indices=idx, num_workers=1)
+    o_d, l_d = run_gpu(w, num_workers=1)
+    np.testing.assert_array_equal(o_s, o_d)
+    np.testing.assert_array_equal(l_s, l_d)
+
+
+def test_sparse_repeat_bitwise_and_without_lse():
+    w = make_workload(SMALL)
+    t = to_torch(w, torch.device("cuda:0"))
+    dec = make_decoder(w)
+    o1, l1 = run_sparse(w, dec=dec, tensors=t)
+    o2, l2 = run_sparse(w, dec=dec, tensors=t)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    o3, _ = run_sparse(w, dec=dec, tensors=t, with_lse=False)
+    np.testing.assert_array_equal(o1, o3)
+
+
+def test_sparse_error_paths():
+    import mla_latent_cache_decode_amd as m
+    w = make_workload(SMALL)
+    t = to_torch(w, torch.device("cuda:0"))
+    lib = m.load_library()
+    dec = make_decoder(w)
+    B, k = w.spec.batch, w.spec.topk
+    ws = dec.alloc_sparse_workspace(B, k)
+    out = torch.zeros((B, 1, 128, 512), dtype=torch.float32, device="cuda")
+    args = lambda topk, ws_bytes, idx_ptr: (dec._h, t["q"].data_ptr(), t["kv"].data_ptr(),  # noqa: E731
+                                             t["block_table"].data_ptr(), t["seq_lens"].data_ptr(), idx_ptr,
+                                             topk, B, out.data_ptr(), None, ws.data_ptr(), ws_bytes, None)
+    say("sparse error paths")
+    idx = t["indices"].data_ptr()
+    assert lib.mla_decode_sparse_run(*args(0, ws.numel(), idx)) == m.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_decode_sparse_run(*args(k, ws.numel(), None)) == m.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_decode_sparse_run(*args(k, ws.numel(), idx + 2)) == m.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_decode_sparse_run(*args(k, 64, idx)) == m.MLA_ERR_WORKSPACE_TOO_SMALL
+    # a larger topk needs a larger workspace
+    assert dec.sparse_workspace_size(B, 4 * k) > dec.sparse_workspace_size(B, k)
+    # the sparse path serves the bf16 cache
+    wf = make_workload("fp8_b64_small")
+    decf = make_decoder(wf)
+    tf = to_torch(wf, torch.device("cuda:0"))
+    idx_f = torch.zeros((wf.spec.batch, 1, 8), dtype=torch.int32, device="cuda")
+    outf = torch.zeros((wf.spec.batch, 1, 128, 512), dtype=torch.float32, device="cuda")
+    wsf = decf.alloc_sparse_workspace(wf.spec.batch, 8)
+    assert lib.mla_decode_sparse_run(decf._h, tf["q"].data_ptr(), tf["kv"].data_ptr(), tf["block_table"].data_ptr(),
+                                     tf["seq_lens"].data_ptr(), idx_f.data_ptr(), 8, wf.spec.batch,
+                                     outf.data_ptr(), None, wsf.data_ptr(), wsf.numel(),
+                                     None) == m.MLA_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0 and torch.count_nonzero(outf).item() == 0
