@@ -29,7 +29,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // last split, so a batch never branches around its loads (branches would
 // make the compiler wait for every load at the join) and the lanes of a
 // short batch read zeros without touching memory.
-constexpr int kLoadBatch = 16;      // partial rows in flight per wave
 
 __device__ __forceinline__ float wave_max(float v) {
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -72,8 +71,12 @@ __device__ __forceinline__ void store_row(const CombineArgs& a, int b, int row, 
     if (a.lse && t == 0) a.lse[(int64_t)b * a.rows + row] = dead ? -__builtin_inff() : mx + logf(sum);
 }
 
-template <int WPR, int RPB>
+// LB: partial rows in flight per wave (16 when a row's splits are many; 8
+// when they are few, which halves the registers and doubles the waves in
+// flight)
+template <int WPR, int RPB, int LB>
 __global__ __launch_bounds__(WPR * RPB * 64) void combine_kernel(CombineArgs a) {
+    constexpr int kLoadBatch = LB;
     // partial sums of waves 1 .. WPR - 1 of each row, reduced by its wave 0
     __shared__ f32x4 s_acc[WPR > 1 ? RPB * (WPR - 1) * 2 * 64 : 1];
     const int M = a.rows;                                 // a multiple of 32, so of RPB
@@ -176,9 +179,13 @@ hipError_t launch_combine(const CombineArgs& a, int max_splits, hipStream_t stre
     // expected splits per sequence: the workers spread over the batch
     const int per_seq = max_splits / max(a.batch, 1);
     if (per_seq >= 32) {
-        hipLaunchKernelGGL((combine_kernel<8, 1>), dim3((unsigned)(a.batch * a.rows)), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((combine_kernel<8, 1, 16>), dim3((unsigned)(a.batch * a.rows)), dim3(512), 0, stream, a);
+    } else if (per_seq >= 6) {
+        // lengths vary: the longest sequences have about twice the mean split count
+        hipLaunchKernelGGL((combine_kernel<1, 4, 16>), dim3((unsigned)(a.batch * (a.rows / 4))), dim3(256), 0,
+                           stream, a);
     } else {
-        hipLaunchKernelGGL((combine_kernel<1, 4>), dim3((unsigned)(a.batch * (a.rows / 4))), dim3(256), 0, stream,
+        hipLaunchKernelGGL((combine_kernel<1, 4, 8>), dim3((unsigned)(a.batch * (a.rows / 4))), dim3(256), 0, stream,
                            a);
     }
     return hipGetLastError();
