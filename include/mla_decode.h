@@ -168,8 +168,7 @@ mla_status_t mla_decode_sparse_workspace_size(mla_decode_handle_t h, int32_t bat
  *   every other argument as for mla_decode_run (the handle's s_q, n_h,
  *   block_size and softmax scale apply); workspace >=
  *   mla_decode_sparse_workspace_size(batch, topk) bytes.
- * The handle must be for a bf16 cache (fp8: MLA_ERR_UNSUPPORTED).  Enqueues
- * three kernels on the stream: the pre-pass that turns index lists into
+ * Both cache formats are served.  Enqueues three kernels on the stream: the pre-pass that turns index lists into
  * physical row ids (through the block table) and masks, the decode that
  * gathers those rows, and the split combine.  Only the listed rows are read;
  * the block-table entries of listed valid tokens must be valid pages. */

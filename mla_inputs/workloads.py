@@ -118,6 +118,10 @@ SPECS = {
     # longer than topk, bf16 paged cache
     "sparse_topk2048_b64": WorkloadSpec("sparse_topk2048_b64", 64, ("uniform", 4096, 32768), topk=2048,
                                         seed=6),
+    # the same over the FP8 cache (the format FlashMLA's sparse decode requires,
+    # "DeepSeek-R1" record constraint (2)), with the FP8 recipe's outliers
+    "sparse_fp8_topk2048_b64": WorkloadSpec("sparse_fp8_topk2048_b64", 64, ("uniform", 4096, 32768), topk=2048,
+                                            kv_dtype="fp8", outlier_p=0.01, outlier_mult=20.0, seed=7),
 }
 
 # reduced-size variants of the same recipes for element-by-element parity
@@ -136,6 +140,9 @@ SPECS.update({
     "sparse_topk2048_b64_small": dataclasses.replace(SPECS["sparse_topk2048_b64"], name="sparse_topk2048_b64_small",
                                                      batch=5, seq_lens=("uniform", 100, 3000), topk=700,
                                                      spare_pages=8),
+    "sparse_fp8_topk2048_b64_small": dataclasses.replace(SPECS["sparse_fp8_topk2048_b64"],
+                                                         name="sparse_fp8_topk2048_b64_small", batch=5,
+                                                         seq_lens=("uniform", 100, 3000), topk=700, spare_pages=8),
 })
 
 # the long-context workload is the one the bandwidth target is stated on

@@ -308,7 +308,6 @@ mla_status_t mla_decode_sparse_run(mla_decode_handle_t h, const void* q, const v
     const mla_status_t v = check_run_pointers(q, kv_pages, block_table, seq_lens, out, lse, workspace);
     if (v != MLA_OK) return v;
     if (!indices || !aligned(indices, 4)) return MLA_ERR_INVALID_ARGUMENT;
-    if (h->p.kv_dtype != MLA_KV_BF16) return MLA_ERR_UNSUPPORTED;
     const SparseLayout l = sparse_layout(h, batch, topk);
     if (workspace_bytes < l.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
@@ -347,7 +346,10 @@ mla_status_t mla_decode_sparse_run(mla_decode_handle_t h, const void* q, const v
     da.sparse_zero_row = ra.zero_row;
     const hipEvent_t e0 = h->ev_start && h->ev_stop ? h->ev_start : nullptr;
     const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
-    if (mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1) != hipSuccess) return MLA_ERR_HIP;
+    const hipError_t e = h->p.kv_dtype == MLA_KV_BF16
+                             ? mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1)
+                             : mla::launch_decode_fp8_sparse(da, l.row_groups, stream, e0, e1);
+    if (e != hipSuccess) return MLA_ERR_HIP;
 
     mla::CombineArgs ca{};
     ca.plan = plan;

@@ -103,6 +103,13 @@ struct Fp8Pieces {
         const int scl = pinned(src_lane) - ((l >> 4) << 4) + kD + (l >> 5);
         s.scale = __builtin_amdgcn_raw_buffer_load_b8(r, scl + k * 2, 0, 0);
     }
+    // sparse gather: the lane's token row starts at `row` (anywhere in the
+    // cache, or the workspace's zero row for an entry that does not take part)
+    __device__ __forceinline__ void issue(Stage& s, const uint8_t* row, int, int k) const {
+        const int l = opaque_lane();
+        s.codes = *(const u32x4*)(row + ((l >> 4) << 4) + k * 64);
+        s.scale = row[kD + (l >> 5) + k * 2];
+    }
     __device__ __forceinline__ void store(const Stage& s, LDS_AS uint8_t* tile, int, int k) const {
         // 2^(e-127) as fp32 bits e << 23.  e = 255 (NaN) also sets the top
         // mantissa bit, making a quiet NaN instead of infinity.  e = 0 gives
@@ -143,9 +150,11 @@ struct WaveState {
 // One tile step of one wave.  qk_hook(ks) runs inside Q.K^T step ks and
 // pv_hook(step) inside P.V step `step` (both compile-time); they carry the
 // page pipeline's loads and LDS stores so that these issue between MFMAs.
-template <typename QkHook, typename PvHook>
+// Tokens of the tile that take part: the first n_valid (dense), or the set
+// bits of `mask` (sparse: the pre-pass's tile mask).
+template <bool kSparse, typename QkHook, typename PvHook>
 __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f16x8 (&qf)[kQRegSteps],
-                                             const LDS_AS uint8_t* qr, WaveState& st, int n_valid,
+                                             const LDS_AS uint8_t* qr, WaveState& st, int n_valid, uint64_t mask,
                                              float scale_log2, QkHook&& qk_hook, PvHook&& pv_hook) {
     const int lane = opaque_lane();
     const int hi = lane >> 5;
@@ -186,16 +195,22 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
     // are masked: excluded from the max and given p = 0.  The token of
     // register r is c_r + 4*hi (+32 for s1); compare c_r with nv_lane.
     const int nv_lane = n_valid - (hi << 2);
+    const uint64_t m_lane = mask >> (hi << 2);
+    // does token c + 4 hi of the tile take part (c compile-time)
+    auto vis = [&](int c) -> bool {
+        if constexpr (kSparse) return (m_lane >> c) & 1;
+        else return c < nv_lane;
+    };
     float mx = -__builtin_inff();
-    if (n_valid >= kPage) {
+    if (kSparse ? mask == ~0ull : n_valid >= kPage) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
     } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int c_r = ((r >> 2) << 3) + (r & 3);
-            mx = fmaxf(mx, c_r < nv_lane ? s0[r] : -__builtin_inff());
-            mx = fmaxf(mx, c_r + 32 < nv_lane ? s1[r] : -__builtin_inff());
+            mx = fmaxf(mx, vis(c_r) ? s0[r] : -__builtin_inff());
+            mx = fmaxf(mx, vis(c_r + 32) ? s1[r] : -__builtin_inff());
         }
     }
     mx = pair_max(mx);
@@ -227,7 +242,7 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
         for (int e = 0; e < 8; ++e) {
             const int r = (kb & 1) * 8 + e;
             const int c_r = ((r >> 2) << 3) + (r & 3) + (kb >= 2 ? 32 : 0);
-            const float x = c_r < nv_lane ? fast_exp2(fmaf(sv[r], scale_log2, neg_m)) : 0.f;
+            const float x = vis(c_r) ? fast_exp2(fmaf(sv[r], scale_log2, neg_m)) : 0.f;
             lsum += x;
             f[e] = (_Float16)x;
         }
@@ -289,7 +304,12 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
 // ---------------------------------------------------------------------------
 // the decode kernel
 // ---------------------------------------------------------------------------
-template <int PS>
+// kSparse: the top-k decode ("DeepSeek-V3.2" record): a unit (one query
+// position, n_h rows) attends to the rows its index list selects; each lane
+// gathers its token's row through the pre-pass's row table (entries that
+// do not take part read the workspace's zero row) and the pre-pass's tile
+// mask takes the place of the length mask.
+template <int PS, bool kSparse>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArgs a) {
     typedef Fp8Pieces Pieces;
     typedef PageGeom<PS> Geom;
@@ -326,7 +346,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
     int64_t cost = start.cost;
     int slot_base = start.slot;
     for (int b = start.b; b < a.batch; ++b) {
-        const int L = ld_const(a.seq_lens + b);
+        const int L = kSparse ? a.sparse_topk : ld_const(a.seq_lens + b);
         const int pages = L > 0 ? (L + kPage - 1) / kPage : 0;
         if (pages == 0) continue;
         const int64_t A = cost + a.overhead_units, E = A + pages;
@@ -354,16 +374,49 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         const __amdgpu_buffer_rsrc_t bt = make_rsrc((const uint8_t*)(a.block_table + (int64_t)b * a.max_blocks),
                                                     (PS < kPage ? min(Geom::entries(p_hi), a.max_blocks)
                                                                 : Geom::entries(p_hi)) * 4);
+        // sparse: row table and tile masks of this unit (tiles at or past
+        // p_hi read zeros and are not used)
+        const int64_t tiles_u = kSparse ? pages : 0;
+        const __amdgpu_buffer_rsrc_t r_rows =
+            make_rsrc((const uint8_t*)(a.sparse_rows + (kSparse ? (int64_t)b * tiles_u * 64 : 0)), p_hi * 256);
+        const __amdgpu_buffer_rsrc_t r_mask =
+            make_rsrc((const uint8_t*)(a.sparse_masks + (kSparse ? (int64_t)b * tiles_u : 0)), p_hi * 8);
+        // dense: the block-table entry of tile p's page for this wave;
+        // sparse: the row id of this lane's token of tile p (token 16w + (i & 15)
+        // sits in the table's pair (w * 8 + (i & 7)), element (i >> 3) & 1)
         auto load_phys = [&](int p) -> int {
-            return __builtin_amdgcn_raw_buffer_load_b32(bt, Geom::entry(p, tok0) * 4, 0, 0);
+            if constexpr (kSparse) {
+                const int l = pinned(tid & 63);
+                return __builtin_amdgcn_raw_buffer_load_b32(
+                    r_rows, p * 256 + ((wave * 8 + (l & 7)) * 2 + ((l >> 3) & 1)) * 4, 0, 0);
+            } else {
+                return __builtin_amdgcn_raw_buffer_load_b32(bt, Geom::entry(p, tok0) * 4, 0, 0);
+            }
         };
-        // descriptor over the rows of tile p in the wave's page (physical
-        // page phys) that the workgroup loads; size 0 past p_hi
+        auto load_mask = [&](int p) -> u32x2 {
+            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r_mask, p * 8, 0, 0));
+        };
+        // dense: descriptor over the rows of tile p in the wave's page
+        // (physical page phys) that the workgroup loads, size 0 past p_hi;
+        // sparse: the lane's row (row id phys), or the zero row
         auto page_rsrc = [&](int p, int phys) {
-            const int nv = p < p_hi ? min(max(n_load - p * kPage - tok0, 0), Geom::kRangeTok) : 0;
-            return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes +
-                                 Geom::row_in_page(p, tok0) * kRowBytes,
-                             nv * kRowBytes);
+            if constexpr (kSparse) {
+                const bool live = p < p_hi && (uint32_t)phys != kNoRow;
+                return live ? a.kv + (uint64_t)(uint32_t)phys * kRowBytes : a.sparse_zero_row;
+            } else {
+                const int nv = p < p_hi ? min(max(n_load - p * kPage - tok0, 0), Geom::kRangeTok) : 0;
+                return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes +
+                                     Geom::row_in_page(p, tok0) * kRowBytes,
+                                 nv * kRowBytes);
+            }
+        };
+        typedef decltype(page_rsrc(0, 0)) Src;
+        // a tile mask loaded as two words, made wave-uniform (each word
+        // through uint32: readfirstlane's int would sign-extend into the
+        // upper word)
+        auto join_mask = [](const u32x2& v) -> uint64_t {
+            return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(v[1]) << 32) |
+                   (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(v[0]);
         };
 
         // this wave's 32 query rows as MFMA B operands (q_abs || q_R): bf16
@@ -436,7 +489,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
                 static_assert(last < Pieces::kHookAt[h + 1], "hooks of a phase must not overlap");
         });
 
-        const __amdgpu_buffer_rsrc_t r0 = page_rsrc(p_lo, phys0);
+        const Src r0 = page_rsrc(p_lo, phys0);
         Stage stg[kS], s0p[kPieces];
         static_for<0, kPieces>([&](auto k) { pc.issue(s0p[k], r0, wave, k); });
         {
@@ -445,8 +498,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
 #pragma unroll
             for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = __builtin_bit_cast(f16x8, *(const bf16x8*)(qrow + ks * 16));
         }
-        __amdgpu_buffer_rsrc_t r_next = page_rsrc(p_lo + 1, phys1);
+        Src r_next = page_rsrc(p_lo + 1, phys1);
         int phys2 = load_phys(p_lo + 2);
+        // sparse: masks of the current and the next tile (loaded two ahead)
+        uint64_t mask_cur = ~0ull, mask_next = ~0ull;
+        u32x2 mkv0, mkv1;
+        if constexpr (kSparse) {
+            mkv0 = load_mask(p_lo);
+            mkv1 = load_mask(p_lo + 1);
+        }
         st.m = -__builtin_inff();
         st.l = 0.f;
         st.o_zero = true;
@@ -457,6 +517,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
             if constexpr (k < Pieces::first(1)) pc.issue(stg[k], r_next, wave, k);   // batch 0 of page p_lo + 1
         });
         convert_q();
+        if constexpr (kSparse) {
+            mask_cur = join_mask(mkv0);
+            mask_next = join_mask(mkv1);
+        }
         __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
         wg_barrier();
 
@@ -464,7 +528,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
             const LDS_AS uint8_t* tile = tiles[(p - p_lo) & 1];
             LDS_AS uint8_t* tnext = tiles[(p - p_lo + 1) & 1];
             const int phys_next = load_phys(p + 3);
-            __amdgpu_buffer_rsrc_t r2;
+            u32x2 mkv_after;
+            if constexpr (kSparse) mkv_after = load_mask(p + 2);
+            Src r2;
             // hook h, slot k: store piece k of batch h (page p + 1) and load
             // piece k of the next batch into the freed slot; the last batch
             // is followed by batch 0 of page p + 2
@@ -498,10 +564,14 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
                         move_piece(h_c, std::integral_constant<int, (step - at) / sd>{});
                 });
             };
-            compute_tile(tile, qreg, qr_lds, st, min(max(n_vis - p * kPage, 0), kPage), scale_lane, qk_hook,
-                         pv_hook);
+            compute_tile<kSparse>(tile, qreg, qr_lds, st, min(max(n_vis - p * kPage, 0), kPage), mask_cur, scale_lane,
+                                  qk_hook, pv_hook);
             r_next = r2;
             phys2 = phys_next;
+            if constexpr (kSparse) {
+                mask_cur = mask_next;
+                mask_next = join_mask(mkv_after);
+            }
             __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);       // tile stores and reads retired
             wg_barrier();
         }
@@ -546,13 +616,20 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t st
                              hipEvent_t ev_stop) {
     const dim3 grid(a.num_workers * row_groups), block(kDecodeThreads);
     switch (a.page_size) {
-        case 16: hipExtLaunchKernelGGL(mla_decode_kernel<16>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 32: hipExtLaunchKernelGGL(mla_decode_kernel<32>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 64: hipExtLaunchKernelGGL(mla_decode_kernel<64>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 128: hipExtLaunchKernelGGL(mla_decode_kernel<128>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 256: hipExtLaunchKernelGGL(mla_decode_kernel<256>, grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 16: hipExtLaunchKernelGGL((mla_decode_kernel<16, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 32: hipExtLaunchKernelGGL((mla_decode_kernel<32, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 64: hipExtLaunchKernelGGL((mla_decode_kernel<64, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 128: hipExtLaunchKernelGGL((mla_decode_kernel<128, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 256: hipExtLaunchKernelGGL((mla_decode_kernel<256, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                                    hipEvent_t ev_stop) {
+    hipExtLaunchKernelGGL((mla_decode_kernel<64, true>), dim3(a.num_workers * row_groups), dim3(kDecodeThreads), 0,
+                          stream, ev_start, ev_stop, 0, a);
     return hipGetLastError();
 }
 

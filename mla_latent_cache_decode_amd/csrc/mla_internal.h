@@ -106,6 +106,8 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t st
                              hipEvent_t ev_stop);
 hipError_t launch_decode_bf16_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                                      hipEvent_t ev_stop);
+hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                                    hipEvent_t ev_stop);
 hipError_t launch_sparse_rows(const SparseRowsArgs& a, hipStream_t stream);
 // max_splits: an upper bound on the splits of one sequence (the worker
 // count); it sizes the combine's LDS and picks its shape.

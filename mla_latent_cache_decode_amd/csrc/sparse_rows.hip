@@ -34,7 +34,8 @@ __global__ __launch_bounds__(64) void sparse_rows_kernel(SparseRowsArgs a) {
     dst[(w * 8 + x) * 2 + g] = row;
     if (lane == 0) a.masks[(int64_t)u * a.tiles + p] = mask;
     // the row the decode fetches for entries that do not take part (their
-    // weights are 0, and 0 x 0 keeps the product finite whatever the data)
+    // weights are 0, and 0 x 0 keeps the product finite whatever the data;
+    // as an fp8 row its codes and scales are 0 too, so it decodes to zeros)
     if (blockIdx.x == 0) {
         for (int i = lane; i < kSparseZeroRowBytes / 16; i += 64)
             *(uint4*)(a.zero_row + i * 16) = make_uint4(0, 0, 0, 0);

@@ -185,6 +185,13 @@ EDGE = [
     WorkloadSpec("edge_heads256", 2, ("fixed", (129, 640)), n_h=256, spare_pages=2, seed=16),
     WorkloadSpec("edge_mtp4", 3, ("fixed", (3, 66, 257)), s_q=4, spare_pages=2, seed=17),
     WorkloadSpec("edge_empty_seq", 3, ("fixed", (0, 70, 0)), spare_pages=2, seed=18),
+    # flat softmax (q = 0, or nearly): every visible token weighs the same, so
+    # a token wrongly counted or dropped by a mask moves the output by about
+    # 1/n, far past the tolerance
+    WorkloadSpec("edge_flat_q0", 5, ("fixed", (1, 36, 100, 700, 1500)), q_scale=0.0, spare_pages=4, seed=19),
+    WorkloadSpec("edge_flat_q0_fp8", 5, ("fixed", (1, 36, 100, 700, 1500)), q_scale=0.0, kv_dtype="fp8",
+                 spare_pages=4, seed=20),
+    WorkloadSpec("edge_flat_mtp", 4, ("fixed", (2, 37, 101, 701)), q_scale=0.02, s_q=2, spare_pages=4, seed=24),
 ]
 
 

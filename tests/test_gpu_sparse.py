@@ -46,6 +46,16 @@ VARIANTS = [
     dataclasses.replace(SMALL, name="sparse_page32_small", page=32, seed=44),
     dataclasses.replace(SMALL, name="sparse_topk64_small", topk=64, seed=45),
     dataclasses.replace(SMALL, name="sparse_topk1_small", topk=1, seed=46),
+    SPECS["sparse_fp8_topk2048_b64_small"],
+    dataclasses.replace(SPECS["sparse_fp8_topk2048_b64_small"], name="sparse_fp8_mtp2_small", s_q=2, seed=50),
+    dataclasses.replace(SPECS["sparse_fp8_topk2048_b64_small"], name="sparse_fp8_page32_small", page=32, seed=51),
+    # flat softmax: a token wrongly counted or dropped by the tile mask moves
+    # the output by about 1/n (the lists here are shorter than 64 tokens past
+    # the last full tile, both tile halves partly valid)
+    dataclasses.replace(SMALL, name="sparse_flat_q0", q_scale=0.0, seq_lens=("fixed", (100, 36, 700, 2000, 1)),
+                        topk=700, seed=52),
+    dataclasses.replace(SPECS["sparse_fp8_topk2048_b64_small"], name="sparse_fp8_flat_q0", q_scale=0.0,
+                        seq_lens=("fixed", (100, 36, 700, 2000, 1)), topk=700, seed=53),
 ]
 
 
@@ -58,8 +68,9 @@ def test_sparse_parity_small(spec, workers):
     assert_parity(w, out, lse, ro, rl)
 
 
-def test_sparse_full_size_sampled():
-    w = make_workload("sparse_topk2048_b64")
+@pytest.mark.parametrize("name", ["sparse_topk2048_b64", "sparse_fp8_topk2048_b64"])
+def test_sparse_full_size_sampled(name):
+    w = make_workload(name)
     batches = sorted({0, 31, 63, int(np.argmax(w.seq_lens))})
     out, lse = run_sparse(w)
     ro, rl = sparse_oracle(w, batches=batches)
@@ -83,9 +94,11 @@ def test_sparse_ignores_entries_outside_the_context():
     assert_parity(w, out, lse, ro, rl)
 
 
-def test_sparse_reads_only_selected_rows():
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_sparse_reads_only_selected_rows(kv_dtype):
     # every row no list selects is NaN-poisoned: bitwise the same result
-    w = make_workload(dataclasses.replace(SMALL, name="sparse_poison", seed=48))
+    base = SMALL if kv_dtype == "bf16" else SPECS["sparse_fp8_topk2048_b64_small"]
+    w = make_workload(dataclasses.replace(base, name=f"sparse_poison_{kv_dtype}", seed=48))
     o1, l1 = run_sparse(w, num_workers=7)
     used = np.zeros(w.pool.shape[:2], dtype=bool)
     for b in range(w.spec.batch):
@@ -93,17 +106,19 @@ def test_sparse_reads_only_selected_rows():
             if 0 <= t < int(w.seq_lens[b]):
                 used[w.block_table[b, t // 64], t % 64] = True
     pool = w.pool.copy()
-    pool[~used] = 0x7FC0
+    pool[~used] = 0x7FC0 if kv_dtype == "bf16" else 0x7F
     o2, l2 = run_sparse(dataclasses.replace(w, pool=pool), num_workers=7)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
 
 
-def test_sparse_over_whole_context_equals_dense_bitwise():
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_sparse_over_whole_context_equals_dense_bitwise(kv_dtype):
     # index lists 0 .. L-1 in order (padded with -1) visit the dense decode's
     # tiles in the dense order; with one worker neither run splits, so the
     # two must agree bit for bit
-    spec = WorkloadSpec("sparse_vs_dense", 3, ("fixed", (700, 64, 1500)), topk=1500, spare_pages=4, seed=49)
+    spec = WorkloadSpec(f"sparse_vs_dense_{kv_dtype}", 3, ("fixed", (700, 64, 1500)), topk=1500, spare_pages=4,
+                        seed=49, kv_dtype=kv_dtype, outlier_p=0.01, outlier_mult=20.0)
     w = make_workload(spec)
     idx = np.full_like(w.indices, -1)
     for b in range(spec.batch):
@@ -146,16 +161,6 @@ def test_sparse_error_paths():
     assert lib.mla_decode_sparse_run(*args(k, 64, idx)) == m.MLA_ERR_WORKSPACE_TOO_SMALL
     # a larger topk needs a larger workspace
     assert dec.sparse_workspace_size(B, 4 * k) > dec.sparse_workspace_size(B, k)
-    # the sparse path serves the bf16 cache
-    wf = make_workload("fp8_b64_small")
-    decf = make_decoder(wf)
-    tf = to_torch(wf, torch.device("cuda:0"))
-    idx_f = torch.zeros((wf.spec.batch, 1, 8), dtype=torch.int32, device="cuda")
-    outf = torch.zeros((wf.spec.batch, 1, 128, 512), dtype=torch.float32, device="cuda")
-    wsf = decf.alloc_sparse_workspace(wf.spec.batch, 8)
-    assert lib.mla_decode_sparse_run(decf._h, tf["q"].data_ptr(), tf["kv"].data_ptr(), tf["block_table"].data_ptr(),
-                                     tf["seq_lens"].data_ptr(), idx_f.data_ptr(), 8, wf.spec.batch,
-                                     outf.data_ptr(), None, wsf.data_ptr(), wsf.numel(),
-                                     None) == m.MLA_ERR_UNSUPPORTED
+    assert lib.mla_decode_sparse_run(*args((1 << 20) + 1, ws.numel(), idx)) == m.MLA_ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
-    assert torch.count_nonzero(out).item() == 0 and torch.count_nonzero(outf).item() == 0
+    assert torch.count_nonzero(out).item() == 0
