@@ -206,6 +206,17 @@ def main():
     fl = flops_per_step(w)
     tflops = fl / (ms_step * 1e-3) / 1e12
     k_gbs = kv_bytes / (kms * 1e-3) / 1e9
+    k_tflops = fl / (kms * 1e-3) / 1e12
+    # the kernel's roofline: HBM below the balance point (2.5 PFLOP/s over
+    # 8 TB/s = 312.5 flop/B), the matrix cores above it (the products run as
+    # 16-bit MFMA for both cache formats, so the 16-bit peak applies)
+    intensity = fl / kv_bytes
+    if intensity <= BF16_MFMA_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        roof = {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(k_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
     info = dec.info()
     from mla_latent_cache_decode_amd.rocprof_summary import kernel_for_dtype
     kernel = kernel_for_dtype(s.kv_dtype)
@@ -221,7 +232,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if s.kv_dtype == "bf16" else "fp8-e4m3/e8m0 cache, bf16 mfma",
+        "dtype": "bf16" if s.kv_dtype == "bf16" else "fp8-e4m3/e8m0 cache, fp16 mfma",
         "data": "synthetic (seeded N(0,1) cache and queries, DeepSeek-V3/R1 shapes)",
         "config": {"workload": s.name, "batch": s.batch, "s_q": s.s_q, "n_h": s.n_h, "d_c": s.d_c,
                    "d_r": s.d_r, "page": s.page, "kv_dtype": s.kv_dtype,
@@ -233,11 +244,11 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tflop_s": round(tflops, 2),
         "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-        "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+        "roofline": {**roof,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
                      "kernel": kernel, "kernel_ms": round(kms, 5), "kernel_samples": len(kernel_ms),
-                     "bytes_per_launch": kv_bytes},
+                     "bytes_per_launch": kv_bytes, "flop_per_launch": fl,
+                     "intensity_flop_per_byte": round(intensity, 1), "kernel_gbs": round(k_gbs, 2)},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
