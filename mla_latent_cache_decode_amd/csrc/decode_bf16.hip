@@ -676,24 +676,21 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                               hipEvent_t ev_stop) {
-    const dim3 grid(a.num_workers * row_groups), block(kDecodeThreads);
+    const dim3 grid(a.num_workers * row_groups);
     switch (a.page_size) {
-        case 16: hipExtLaunchKernelGGL((mla_decode_bf16_kernel<16, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 32: hipExtLaunchKernelGGL((mla_decode_bf16_kernel<32, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 64: hipExtLaunchKernelGGL((mla_decode_bf16_kernel<64, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 128: hipExtLaunchKernelGGL((mla_decode_bf16_kernel<128, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
-        case 256: hipExtLaunchKernelGGL((mla_decode_bf16_kernel<256, false>), grid, block, 0, stream, ev_start, ev_stop, 0, a); break;
+        case 16: return launch_with_events(mla_decode_bf16_kernel<16, false>, grid, stream, ev_start, ev_stop, a);
+        case 32: return launch_with_events(mla_decode_bf16_kernel<32, false>, grid, stream, ev_start, ev_stop, a);
+        case 64: return launch_with_events(mla_decode_bf16_kernel<64, false>, grid, stream, ev_start, ev_stop, a);
+        case 128: return launch_with_events(mla_decode_bf16_kernel<128, false>, grid, stream, ev_start, ev_stop, a);
+        case 256: return launch_with_events(mla_decode_bf16_kernel<256, false>, grid, stream, ev_start, ev_stop, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_decode_bf16_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                                      hipEvent_t ev_stop) {
     // the gather goes through the row table: the page-block size is the pre-pass's business
-    hipExtLaunchKernelGGL((mla_decode_bf16_kernel<64, true>), dim3(a.num_workers * row_groups), dim3(kDecodeThreads),
-                          0, stream, ev_start, ev_stop, 0, a);
-    return hipGetLastError();
+    return launch_with_events(mla_decode_bf16_kernel<64, true>, dim3(a.num_workers * row_groups), stream, ev_start, ev_stop, a);
 }
 
 }  // namespace mla

@@ -326,5 +326,18 @@ __device__ __forceinline__ void block_role(int G, int& worker, int& rg) {
     }
 }
 
+// Launch a decode kernel: with profile events, through the dispatch that
+// records its own start and end timestamps into them; otherwise a plain
+// launch (what a captured HIP graph then holds).
+template <typename Kernel>
+hipError_t launch_with_events(Kernel kernel, dim3 grid, hipStream_t stream, hipEvent_t ev_start,
+                              hipEvent_t ev_stop, const DecodeArgs& a) {
+    if (ev_start && ev_stop)
+        hipExtLaunchKernelGGL(kernel, grid, dim3(kDecodeThreads), 0, stream, ev_start, ev_stop, 0, a);
+    else
+        hipLaunchKernelGGL(kernel, grid, dim3(kDecodeThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace mla
