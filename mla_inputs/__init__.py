@@ -14,6 +14,9 @@ from .workloads import (  # noqa: F401
     BENCH_SPEC,
     make_workload,
     quantize_fp8_rows,
+    E2M1_MAGNITUDES,
+    quantize_fp4_rows,
     fp8_row_stride,
+    fp4_row_stride,
     to_torch,
 )

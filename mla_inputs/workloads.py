@@ -12,8 +12,8 @@ Draw order (torch CPU generator, seeded per workload):
   1. seq_lens
   2. physical page permutation (unless the table is the identity)
   3. cache source values: float32 N(0,1), drawn in chunks of 256 pages
-     (for FP8 first an outlier mask per chunk, then the values), then
-     rounded to bf16 (round-to-nearest-even) or quantised to FP8
+     (for FP8 / FP4 first an outlier mask per chunk, then the values), then
+     rounded to bf16 (round-to-nearest-even) or quantised to FP8 / FP4
   4. queries: float32 N(0,1) times the workload's q scale, rounded to bf16
   5. sparse workloads only ("DeepSeek-V3.2" record: a top-k selector,
      index_topk = 2048, picks the tokens each query attends over): for every
@@ -39,6 +39,7 @@ import torch
 BF16_NAN = 0x7FC0
 FP8_CODE_NAN = 0x7F
 E8M0_NAN = 0xFF
+FP4_CODE_POISON = 0x77          # two codes of magnitude 6; e2m1 has no NaN
 GEN_CHUNK_PAGES = 256
 
 
@@ -47,7 +48,7 @@ class WorkloadSpec:
     name: str
     batch: int
     seq_lens: Union[Tuple[str, int, int], Tuple[str, Tuple[int, ...]]]
-    kv_dtype: str = "bf16"          # "bf16" | "fp8"
+    kv_dtype: str = "bf16"          # "bf16" | "fp8" | "fp4"
     s_q: int = 1
     n_h: int = 128
     d_c: int = 512
@@ -90,8 +91,15 @@ class Workload:
     @property
     def kv_bytes_algorithmic(self) -> int:
         """Bytes of cache payload the decode must read: rows read x row payload."""
-        per_row = 2 * self.spec.d if self.spec.kv_dtype == "bf16" else self.spec.d + self.spec.d // 32
+        d = self.spec.d
+        per_row = {"bf16": 2 * d, "fp8": d + d // 32, "fp4": d // 2 + d // 16}[self.spec.kv_dtype]
         return self.selected_tokens * per_row
+
+
+def fp4_row_stride(d: int) -> int:
+    """FP4 row stride: payload (d/2 code bytes + d/16 scales) rounded up to 16 bytes."""
+    payload = d // 2 + d // 16
+    return (payload + 15) // 16 * 16
 
 
 def fp8_row_stride(d: int) -> int:
@@ -120,6 +128,10 @@ SPECS = {
                                         seed=6),
     # the same over the FP8 cache (the format FlashMLA's sparse decode requires,
     # "DeepSeek-R1" record constraint (2)), with the FP8 recipe's outliers
+    # the fp4 variant of the latent row ("DeepSeek-R1" record, constraint (2):
+    # 288 B per token at 512 dims; 324 B here at 576), same recipe as fp8_b64
+    "fp4_b64": WorkloadSpec("fp4_b64", 64, ("uniform", 2048, 16384), kv_dtype="fp4",
+                            outlier_p=0.01, outlier_mult=20.0, seed=8),
     "sparse_fp8_topk2048_b64": WorkloadSpec("sparse_fp8_topk2048_b64", 64, ("uniform", 4096, 32768), topk=2048,
                                             kv_dtype="fp8", outlier_p=0.01, outlier_mult=20.0, seed=7),
 }
@@ -140,6 +152,8 @@ SPECS.update({
     "sparse_topk2048_b64_small": dataclasses.replace(SPECS["sparse_topk2048_b64"], name="sparse_topk2048_b64_small",
                                                      batch=5, seq_lens=("uniform", 100, 3000), topk=700,
                                                      spare_pages=8),
+    "fp4_b64_small": dataclasses.replace(SPECS["fp4_b64"], name="fp4_b64_small", batch=5,
+                                         seq_lens=("uniform", 100, 2100), spare_pages=8),
     "sparse_fp8_topk2048_b64_small": dataclasses.replace(SPECS["sparse_fp8_topk2048_b64"],
                                                          name="sparse_fp8_topk2048_b64_small", batch=5,
                                                          seq_lens=("uniform", 100, 3000), topk=700, spare_pages=8),
@@ -190,6 +204,42 @@ def quantize_fp8_rows(x: torch.Tensor, d: int, stride: int) -> np.ndarray:
     return out
 
 
+# e2m1 (OCP FP4) magnitudes in code order 0..7 (sign in bit 3); code i has
+# mantissa bit i & 1, so round-to-nearest-even prefers even codes on ties
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def quantize_fp4_rows(x: torch.Tensor, d: int, stride: int) -> np.ndarray:
+    """Encode float32 rows [N, d] into FP4 cache rows [N, stride] (uint8).
+
+    Per row and per group of 16 consecutive values: e = ceil(log2(amax/6))
+    + 127 clamped to [0, 254] (127 when the group is all zero); each value
+    divided by 2^(e-127) is rounded to the nearest e2m1 magnitude (ties to
+    the even code) with its sign in bit 3; codes are packed two per byte,
+    element 2i in the low nibble of byte i.  Then the d/16 scale bytes;
+    padding bytes are set to 0xFF.
+    """
+    n = x.shape[0]
+    g = x.reshape(n, d // 16, 16).to(torch.float64).numpy()
+    amax = np.abs(g).max(axis=-1)
+    mant, ex = np.frexp(amax / 6.0)
+    ceil_log2 = np.where(mant == 0.5, ex - 1, ex).astype(np.int64)
+    e = np.clip(ceil_log2 + 127, 0, 254)
+    e = np.where(amax == 0, 127, e)
+    y = g / np.ldexp(1.0, e - 127)[..., None]
+    dist = np.abs(np.abs(y)[..., None] - E2M1_MAGNITUDES)            # [n, groups, 16, 8]
+    best = dist.min(axis=-1, keepdims=True)
+    ties = dist == best
+    # the lowest even index among the nearest, else the nearest
+    even = np.where(ties & (np.arange(8) % 2 == 0), np.arange(8), 99).min(axis=-1)
+    idx = np.where(even < 99, even, ties.argmax(axis=-1))
+    codes = (idx | np.where(y < 0, 8, 0)).astype(np.uint8).reshape(n, d)
+    out = np.full((n, stride), E8M0_NAN, dtype=np.uint8)
+    out[:, :d // 2] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    out[:, d // 2:d // 2 + d // 16] = e.astype(np.uint8)
+    return out
+
+
 def make_workload(spec: Union[str, WorkloadSpec], seed: Optional[int] = None) -> Workload:
     if isinstance(spec, str):
         spec = SPECS[spec]
@@ -222,12 +272,17 @@ def make_workload(spec: Union[str, WorkloadSpec], seed: Optional[int] = None) ->
         row_stride = fp8_row_stride(d)
         pool = np.full((pool_pages, page, row_stride), E8M0_NAN, dtype=np.uint8)
         pool[:, :, :d] = FP8_CODE_NAN
+    elif spec.kv_dtype == "fp4":
+        # e2m1 has no NaN: poisoned rows carry NaN scales (and the largest codes)
+        row_stride = fp4_row_stride(d)
+        pool = np.full((pool_pages, page, row_stride), E8M0_NAN, dtype=np.uint8)
+        pool[:, :, :d // 2] = FP4_CODE_POISON
     else:
         raise ValueError(spec.kv_dtype)
     for c0 in range(0, n_used, GEN_CHUNK_PAGES):
         c1 = min(c0 + GEN_CHUNK_PAGES, n_used)
         rows = (c1 - c0) * page
-        if spec.kv_dtype == "fp8" and spec.outlier_p > 0:
+        if spec.kv_dtype in ("fp8", "fp4") and spec.outlier_p > 0:
             mask = torch.rand((rows, d), generator=gen) < spec.outlier_p
             vals = torch.randn((rows, d), generator=gen)
             vals = torch.where(mask, vals * spec.outlier_mult, vals)
@@ -236,8 +291,11 @@ def make_workload(spec: Union[str, WorkloadSpec], seed: Optional[int] = None) ->
         if spec.kv_dtype == "bf16":
             enc = vals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
             pool[phys[c0:c1]] = enc.reshape(c1 - c0, page, d)
-        else:
+        elif spec.kv_dtype == "fp8":
             enc = quantize_fp8_rows(vals, d, row_stride)
+            pool[phys[c0:c1]] = enc.reshape(c1 - c0, page, row_stride)
+        else:
+            enc = quantize_fp4_rows(vals, d, row_stride)
             pool[phys[c0:c1]] = enc.reshape(c1 - c0, page, row_stride)
 
     # poison tail slots after each sequence's last token
@@ -247,9 +305,12 @@ def make_workload(spec: Union[str, WorkloadSpec], seed: Optional[int] = None) ->
             last = phys[starts[b] + pages_per_seq[b] - 1]
             if spec.kv_dtype == "bf16":
                 pool[last, L % page:, :] = BF16_NAN
-            else:
+            elif spec.kv_dtype == "fp8":
                 pool[last, L % page:, :d] = FP8_CODE_NAN
                 pool[last, L % page:, d:] = E8M0_NAN
+            else:
+                pool[last, L % page:, :d // 2] = FP4_CODE_POISON
+                pool[last, L % page:, d // 2:] = E8M0_NAN
 
     # 4. queries
     qf = torch.randn((spec.batch, spec.s_q, spec.n_h, d), generator=gen) * spec.q_scale

@@ -6,8 +6,9 @@ It walks the same definition as ``oracle.mla`` (guide section 1.1: score =
 scale * (q_abs . c + q_R . k_R), softmax over visible tokens, output the
 softmax-weighted latents) one scalar at a time, with ``math.exp`` and plain
 loops, and reads the cache through its own decoding path: bf16 through
-``struct`` and FP8 through torch's float8_e4m3fn / float8_e8m0fnu dtypes, not
-through the oracle's lookup tables.  It therefore checks the vectorised
+``struct``, FP8 through torch's float8_e4m3fn / float8_e8m0fnu dtypes and FP4
+through its own nibble and exponent arithmetic, not through the oracle's
+lookup tables.  It therefore checks the vectorised
 oracle's gathering, slicing, masking and reductions independently.
 """
 
@@ -31,10 +32,26 @@ def _fp8_row_values(row_bytes, d: int):
     return [codes[i] * scales[i // 32] for i in range(d)]
 
 
+def _fp4_row_values(row_bytes, d: int):
+    # e2m1 written as (2 + m) * 2^(e - 2) for e > 0 and m * 2^-1 for e = 0;
+    # element 2i in the low nibble of byte i; scale byte g for elements 16g..
+    vals = []
+    for i in range(d):
+        byte = int(row_bytes[i // 2])
+        nib = (byte >> (4 * (i % 2))) & 0xF
+        e, m = (nib >> 1) & 3, nib & 1
+        mag = m * 0.5 if e == 0 else (2 + m) * 2.0 ** (e - 2)
+        scale = 2.0 ** (int(row_bytes[d // 2 + i // 16]) - 127)
+        vals.append((-mag if nib & 8 else mag) * scale)
+    return vals
+
+
 def _row_values(pool, page_id: int, slot: int, kv_dtype: str, d: int):
     row = pool[page_id][slot]
     if kv_dtype == "bf16":
         return [_bf16(row[i]) for i in range(d)]
+    if kv_dtype == "fp4":
+        return _fp4_row_values(row, d)
     return _fp8_row_values(row, d)
 
 

@@ -67,6 +67,8 @@ def decode_rows(raw_rows: np.ndarray, kv_dtype: str, d: int) -> np.ndarray:
         return formats.decode_bf16_rows(raw_rows, d)
     if kv_dtype == "fp8":
         return formats.decode_fp8_rows(raw_rows, d)
+    if kv_dtype == "fp4":
+        return formats.decode_fp4_rows(raw_rows, d)
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
 
 

@@ -83,6 +83,60 @@ def test_fp8_row_scale_groups_follow_32_value_blocks():
     assert not np.array_equal(got, wrong)
 
 
+def test_e2m1_codes():
+    from mla_inputs import E2M1_MAGNITUDES, quantize_fp4_rows
+    lut = formats.E2M1_LUT
+    assert lut.shape == (16,) and not np.isnan(lut).any()
+    # sign in bit 3, magnitudes increasing with the code, largest 6
+    np.testing.assert_array_equal(lut[8:], -lut[:8])
+    assert np.all(np.diff(lut[:8]) > 0) and lut.max() == 6.0 and lut[0] == 0.0
+    # the generator's encoder (a magnitude table with round-to-nearest-even)
+    # and the oracle's bit-field decoder are inverse on every code
+    np.testing.assert_array_equal(lut[:8], E2M1_MAGNITUDES)
+    vals = torch.tensor([lut[list(range(16)) * 2]], dtype=torch.float32)     # 32 values, one row
+    enc = quantize_fp4_rows(vals, 32, 32)
+    np.testing.assert_array_equal(formats.decode_fp4_rows(enc, 32)[0], np.asarray(vals[0], dtype=np.float64))
+    # every e2m1 value is an e4m3 value (torch's decoding)
+    e4 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert set(lut.tolist()) <= set(e4[~np.isnan(e4)].tolist())
+
+
+def test_e2m1_ties_round_to_even_codes():
+    from mla_inputs import quantize_fp4_rows
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    expect = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]        # the neighbour with mantissa bit 0
+    # one 32-value row, both 16-value groups with amax 6 (scale 1)
+    x = torch.tensor([mids + [-v for v in mids] + [6.0, 0.0] + [6.0] + [0.0] * 15], dtype=torch.float32)
+    got = formats.decode_fp4_rows(quantize_fp4_rows(x, 32, 32), 32)[0]
+    np.testing.assert_array_equal(got, expect + [-v for v in expect] + [6.0, 0.0] + [6.0] + [0.0] * 15)
+
+
+def test_fp4_row_nibbles_and_scale_groups():
+    # element i: nibble i % 2 of byte i // 2, scale byte i // 16
+    d = 576
+    g = torch.Generator().manual_seed(7)
+    packed = torch.randint(0, 256, (d // 2,), generator=g, dtype=torch.int32).numpy().astype(np.uint8)
+    scales = (np.arange(d // 16) * 2 + 100).astype(np.uint8)
+    row = np.full(336, 0xFF, dtype=np.uint8)           # padding poisoned: must be ignored
+    row[:d // 2] = packed
+    row[d // 2:d // 2 + d // 16] = scales
+    got = formats.decode_fp4_rows(row[None, :], d)[0]
+    sv = torch.from_numpy(scales).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    for i in range(d):
+        code = (int(packed[i // 2]) >> (4 * (i % 2))) & 0xF
+        assert got[i] == formats.E2M1_LUT[code] * sv[i // 16], i
+    # the other nibble order (high nibble first) must not agree
+    wrong = formats.E2M1_LUT[packed >> 4]
+    assert not np.array_equal(got[0::2] / np.repeat(sv, 8), wrong)
+
+
+def test_fp4_row_bytes_match_page_figure():
+    figs = _figures()
+    assert footprint.fp4_row_bytes(512) == figs["fp4_row_bytes_512_dims"]["value"] == 288
+    assert formats.fp4_row_payload_bytes(512) == 288
+    assert footprint.fp4_row_bytes(576) == 324
+
+
 def test_fp8_row_bytes_match_page_layout():
     figs = _figures()
     assert footprint.fp8_row_bytes(512) == figs["fp8_row_bytes_512_dims"]["value"] == 528

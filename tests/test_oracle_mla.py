@@ -28,7 +28,7 @@ from mla_inputs import WorkloadSpec, make_workload
 def _tiny_spec(kv_dtype, s_q, seed, lens=(1, 64, 65, 130), n_h=2):
     return WorkloadSpec(f"tiny_{kv_dtype}_{s_q}", len(lens), ("fixed", tuple(lens)), kv_dtype=kv_dtype,
                         s_q=s_q, n_h=n_h, spare_pages=3, seed=seed,
-                        outlier_p=0.05 if kv_dtype == "fp8" else 0.0, outlier_mult=20.0)
+                        outlier_p=0.05 if kv_dtype != "bf16" else 0.0, outlier_mult=20.0)
 
 
 def _run_oracle(w, **kw):
@@ -42,7 +42,7 @@ def _run_oracle(w, **kw):
 # ----------------------------------------------------------------------------
 
 def pin_brute_force(kv_dtype, s_q):
-    w = make_workload(_tiny_spec(kv_dtype, s_q, seed=100 + s_q + (7 if kv_dtype == "fp8" else 0)))
+    w = make_workload(_tiny_spec(kv_dtype, s_q, seed=100 + s_q + {"bf16": 0, "fp8": 7, "fp4": 13}[kv_dtype]))
     s = w.spec
     out, lse = _run_oracle(w)
     bo, bl = brute.mla_decode_brute(w.q_bits, w.pool, w.block_table, w.seq_lens, kv_dtype=s.kv_dtype,
@@ -130,7 +130,7 @@ def pin_split_merge(seed=4):
 # the real oracle passes every pin
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "fp4"])
 @pytest.mark.parametrize("s_q", [1, 2])
 def test_oracle_matches_brute_force(kv_dtype, s_q):
     pin_brute_force(kv_dtype, s_q)
