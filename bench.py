@@ -79,7 +79,7 @@ def cpu_baseline(w, budget_s: float) -> dict:
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     s = w.spec
-    row_bytes = 2 * s.d if s.kv_dtype == "bf16" else s.d + s.d // 32
+    row_bytes = {"bf16": 2 * s.d, "fp8": s.d + s.d // 32, "fp4": s.d // 2 + s.d // 16}[s.kv_dtype]
     n_seq, tokens, nbytes = 0, 0, 0
     t0 = time.perf_counter()
     while True:
@@ -232,7 +232,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if s.kv_dtype == "bf16" else "fp8-e4m3/e8m0 cache, fp16 mfma",
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3/e8m0 cache, fp16 mfma",
+                  "fp4": "fp4-e2m1/e8m0 cache, fp16 mfma"}[s.kv_dtype],
         "data": "synthetic (seeded N(0,1) cache and queries, DeepSeek-V3/R1 shapes)",
         "config": {"workload": s.name, "batch": s.batch, "s_q": s.s_q, "n_h": s.n_h, "d_c": s.d_c,
                    "d_r": s.d_r, "page": s.page, "kv_dtype": s.kv_dtype,

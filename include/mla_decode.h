@@ -59,7 +59,11 @@ typedef enum mla_status {
  *   no padding, at D = 512).  Padding bytes are never read. */
 typedef enum mla_kv_dtype {
     MLA_KV_BF16 = 0,
-    MLA_KV_FP8_E4M3_E8M0 = 1
+    MLA_KV_FP8_E4M3_E8M0 = 1,   /* D e4m3 codes, then one e8m0 scale per 32 ("DeepSeek-R1"
+                                   record, engine kernel constraint (2))                   */
+    MLA_KV_FP4_E2M1_E8M0 = 2    /* D/2 bytes of e2m1 codes (element 2i in the low nibble of
+                                   byte i), then one e8m0 scale per 16: a reading of the
+                                   same constraint's 288-byte fp4 row at 512 dims          */
 } mla_kv_dtype_t;
 
 /* Flags for mla_decode_params_t.flags */

@@ -25,7 +25,8 @@ MLA_ERR_OUT_OF_MEMORY = 5
 
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3_E8M0 = 1
-KV_DTYPES = {"bf16": MLA_KV_BF16, "fp8": MLA_KV_FP8_E4M3_E8M0}
+MLA_KV_FP4_E2M1_E8M0 = 2
+KV_DTYPES = {"bf16": MLA_KV_BF16, "fp8": MLA_KV_FP8_E4M3_E8M0, "fp4": MLA_KV_FP4_E2M1_E8M0}
 
 # every symbol include/mla_decode.h declares
 EXPORTED_SYMBOLS = (

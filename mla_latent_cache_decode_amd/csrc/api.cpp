@@ -135,11 +135,12 @@ mla_status_t validate_params(const mla_decode_params_t* p) {
     if (p->d_c <= 0 || p->d_r < 0 || p->block_size <= 0) return MLA_ERR_INVALID_ARGUMENT;
     if (p->max_blocks_per_seq < 1) return MLA_ERR_INVALID_ARGUMENT;
     if ((int64_t)p->max_blocks_per_seq * p->block_size > (int64_t)1 << 30) return MLA_ERR_INVALID_ARGUMENT;
-    if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3_E8M0) return MLA_ERR_INVALID_ARGUMENT;
+    if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3_E8M0 && p->kv_dtype != MLA_KV_FP4_E2M1_E8M0)
+        return MLA_ERR_INVALID_ARGUMENT;
     if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
     if (p->num_workers < 0 || p->num_workers > mla::kMaxWorkers) return MLA_ERR_INVALID_ARGUMENT;
     if (p->flags != MLA_FLAG_NONE) return MLA_ERR_INVALID_ARGUMENT;
-    if ((p->d_c + p->d_r) % 32 != 0 && p->kv_dtype == MLA_KV_FP8_E4M3_E8M0) return MLA_ERR_INVALID_ARGUMENT;
+    if ((p->d_c + p->d_r) % 32 != 0 && p->kv_dtype != MLA_KV_BF16) return MLA_ERR_INVALID_ARGUMENT;
     // valid requests outside what this build instantiates
     if (p->d_c != mla::kDc || p->d_r != mla::kDr) return MLA_ERR_UNSUPPORTED;
     if (p->block_size < 16 || p->block_size > 256 || (p->block_size & (p->block_size - 1)) != 0)
@@ -170,6 +171,7 @@ size_t mla_kv_row_bytes(int32_t kv_dtype, int32_t d_c, int32_t d_r) {
     const size_t d = (size_t)d_c + (size_t)d_r;
     if (kv_dtype == MLA_KV_BF16) return 2 * d;
     if (kv_dtype == MLA_KV_FP8_E4M3_E8M0) return d % 32 ? 0 : d + d / 32;
+    if (kv_dtype == MLA_KV_FP4_E2M1_E8M0) return d % 32 ? 0 : d / 2 + d / 16;
     return 0;
 }
 
@@ -212,7 +214,7 @@ mla_status_t mla_decode_init(const mla_decode_params_t* params, mla_decode_handl
     if (log && log[0] == '1') {
         std::fprintf(stderr, "[mla_decode] device %d (%s) CUs=%d rows=%d row_groups=%d workers=%d kv=%s\n",
                      dev, prop.gcnArchName, h->compute_units, h->rows, h->row_groups, h->num_workers,
-                     params->kv_dtype == MLA_KV_BF16 ? "bf16" : "fp8");
+                     params->kv_dtype == MLA_KV_BF16 ? "bf16" : params->kv_dtype == MLA_KV_FP8_E4M3_E8M0 ? "fp8" : "fp4");
     }
     *out = h;
     return MLA_OK;
@@ -275,8 +277,10 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     // profile events (both or neither) take the decode kernel's own timestamps
     const hipEvent_t e0 = h->ev_start && h->ev_stop ? h->ev_start : nullptr;
     const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
-    const hipError_t e = h->p.kv_dtype == MLA_KV_BF16 ? mla::launch_decode_bf16(da, h->row_groups, stream, e0, e1)
-                                                      : mla::launch_decode_fp8(da, h->row_groups, stream, e0, e1);
+    const hipError_t e =
+        h->p.kv_dtype == MLA_KV_BF16
+            ? mla::launch_decode_bf16(da, h->row_groups, stream, e0, e1)
+            : mla::launch_decode_fp8(da, h->row_groups, stream, e0, e1, h->p.kv_dtype == MLA_KV_FP4_E2M1_E8M0);
     if (e != hipSuccess) return MLA_ERR_HIP;
 
     mla::CombineArgs ca{};
@@ -348,7 +352,8 @@ mla_status_t mla_decode_sparse_run(mla_decode_handle_t h, const void* q, const v
     const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
     const hipError_t e = h->p.kv_dtype == MLA_KV_BF16
                              ? mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1)
-                             : mla::launch_decode_fp8_sparse(da, l.row_groups, stream, e0, e1);
+                             : mla::launch_decode_fp8_sparse(da, l.row_groups, stream, e0, e1,
+                                                             h->p.kv_dtype == MLA_KV_FP4_E2M1_E8M0);
     if (e != hipSuccess) return MLA_ERR_HIP;
 
     mla::CombineArgs ca{};

@@ -137,6 +137,62 @@ struct Fp8Pieces {
     }
 };
 
+// fp4 rows (D/2 bytes of e2m1 codes, element 2i in the low nibble of byte i,
+// then one e8m0 scale per 16 values, 16-byte stride).  The same pieces as
+// the fp8 rows: lane i carries token 16w + (i & 15), the 16 values of group
+// j = 4k + (i >> 4) -- 8 code bytes -- and their own scale byte j; they
+// dequantise to tile chunks 2j and 2j + 1 of that token.
+struct Fp4Pieces {
+    static constexpr int kPieces = 9;
+    static constexpr int kBatches = 3;
+    static constexpr int kStage = 3;
+    __device__ static constexpr int first(int b) { return 3 * b; }
+    static constexpr int kHookPv[3] = {0, 0, 1};
+    static constexpr int kHookAt[3] = {2, 22, 12};
+    static constexpr int kHookStride[3] = {5, 5, 10};
+    struct Stage {
+        u32x2 codes;
+        uint32_t scale;
+    };
+
+    int src_lane;       // (token - tok0) * 336 + 8 * (i >> 4), inside the wave's page
+    int dst_lane;       // tile_off(token, 2 * (i >> 4)) without the column block
+
+    __device__ __forceinline__ Fp4Pieces(int lane, int wave, int tok0) {
+        const int t = wave * 16 + (lane & 15);
+        src_lane = (t - tok0) * kFp4RowBytes + ((lane >> 4) << 3);
+        dst_lane = tile_off(t, 2 * (lane >> 4));
+    }
+    __device__ __forceinline__ void issue(Stage& s, __amdgpu_buffer_rsrc_t r, int, int k) const {
+        s.codes = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, pinned(src_lane) + k * 32, 0, 0));
+        const int l = opaque_lane();
+        const int scl = pinned(src_lane) - ((l >> 4) << 3) + kD / 2 + (l >> 4);
+        s.scale = __builtin_amdgcn_raw_buffer_load_b8(r, scl + k * 4, 0, 0);
+    }
+    // sparse gather: the lane's token row starts at `row`
+    __device__ __forceinline__ void issue(Stage& s, const uint8_t* row, int, int k) const {
+        const int l = opaque_lane();
+        s.codes = *(const u32x2*)(row + ((l >> 4) << 3) + k * 32);
+        s.scale = row[kD / 2 + (l >> 4) + k * 4];
+    }
+    __device__ __forceinline__ void store(const Stage& s, LDS_AS uint8_t* tile, int, int k) const {
+        // the e8m0 scale as fp32 bits, as for the fp8 rows
+        const uint32_t e = s.scale & 0xFF;
+        const float scale = __builtin_bit_cast(float, (((e + 1) >> 8) << 22) | (e << 23));
+        LDS_AS uint8_t* d = tile + k * 8192;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            // 8 codes: byte b holds elements 2b (low nibble) and 2b + 1
+            const u32x4 h = {
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(s.codes[c], scale, 0)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(s.codes[c], scale, 1)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(s.codes[c], scale, 2)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(s.codes[c], scale, 3))};
+            *(LDS_AS u32x4*)(d + (dst_lane ^ (c << 4))) = h;
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // per-tile compute of one wave: 32 heads x 64 tokens
 // ---------------------------------------------------------------------------
@@ -309,12 +365,12 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
 // gathers its token's row through the pre-pass's row table (entries that
 // do not take part read the workspace's zero row) and the pre-pass's tile
 // mask takes the place of the length mask.
-template <int PS, bool kSparse>
+template <int PS, bool kSparse, bool kFp4>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArgs a) {
-    typedef Fp8Pieces Pieces;
+    typedef std::conditional_t<kFp4, Fp4Pieces, Fp8Pieces> Pieces;
     typedef PageGeom<PS> Geom;
     constexpr int kPieces = Pieces::kPieces;
-    constexpr int kRowBytes = kFp8RowBytes;
+    constexpr int kRowBytes = kFp4 ? kFp4RowBytes : kFp8RowBytes;
     static_assert(Geom::kRangeTok % 16 == 0, "a wave's 16 tokens lie in one page");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
@@ -610,24 +666,33 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
     }
 }
 
-}  // namespace
-
-hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                             hipEvent_t ev_stop) {
+template <bool kFp4>
+hipError_t launch_decode_quantised(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                                   hipEvent_t ev_stop) {
     const dim3 grid(a.num_workers * row_groups);
     switch (a.page_size) {
-        case 16: return launch_with_events(mla_decode_kernel<16, false>, grid, stream, ev_start, ev_stop, a);
-        case 32: return launch_with_events(mla_decode_kernel<32, false>, grid, stream, ev_start, ev_stop, a);
-        case 64: return launch_with_events(mla_decode_kernel<64, false>, grid, stream, ev_start, ev_stop, a);
-        case 128: return launch_with_events(mla_decode_kernel<128, false>, grid, stream, ev_start, ev_stop, a);
-        case 256: return launch_with_events(mla_decode_kernel<256, false>, grid, stream, ev_start, ev_stop, a);
+        case 16: return launch_with_events(mla_decode_kernel<16, false, kFp4>, grid, stream, ev_start, ev_stop, a);
+        case 32: return launch_with_events(mla_decode_kernel<32, false, kFp4>, grid, stream, ev_start, ev_stop, a);
+        case 64: return launch_with_events(mla_decode_kernel<64, false, kFp4>, grid, stream, ev_start, ev_stop, a);
+        case 128: return launch_with_events(mla_decode_kernel<128, false, kFp4>, grid, stream, ev_start, ev_stop, a);
+        case 256: return launch_with_events(mla_decode_kernel<256, false, kFp4>, grid, stream, ev_start, ev_stop, a);
         default: return hipErrorInvalidValue;
     }
 }
 
+}  // namespace
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                             hipEvent_t ev_stop, bool fp4) {
+    return fp4 ? launch_decode_quantised<true>(a, row_groups, stream, ev_start, ev_stop)
+               : launch_decode_quantised<false>(a, row_groups, stream, ev_start, ev_stop);
+}
+
 hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                                    hipEvent_t ev_stop) {
-    return launch_with_events(mla_decode_kernel<64, true>, dim3(a.num_workers * row_groups), stream, ev_start, ev_stop, a);
+                                    hipEvent_t ev_stop, bool fp4) {
+    const dim3 grid(a.num_workers * row_groups);
+    return fp4 ? launch_with_events(mla_decode_kernel<64, true, true>, grid, stream, ev_start, ev_stop, a)
+               : launch_with_events(mla_decode_kernel<64, true, false>, grid, stream, ev_start, ev_stop, a);
 }
 
 }  // namespace mla

@@ -20,6 +20,10 @@ constexpr int kD = kDc + kDr;                 // 576 elements per cached row
 constexpr int kBf16RowBytes = 2 * kD;         // 1152
 constexpr int kFp8Payload = kD + kD / 32;     // 594
 constexpr int kFp8RowBytes = (kFp8Payload + 15) / 16 * 16;  // 608
+// fp4 row (a reading of the same record's 288-byte fp4 variant at 512 dims):
+// D/2 bytes of e2m1 codes, two per byte, then one e8m0 scale per 16 values
+constexpr int kFp4Payload = kD / 2 + kD / 16;                // 324
+constexpr int kFp4RowBytes = (kFp4Payload + 15) / 16 * 16;  // 336
 constexpr int kRowsPerGroup = 128;            // query rows one workgroup serves
 constexpr int kRowsPerWave = 32;
 constexpr int kDecodeThreads = 256;           // 4 waves of 64
@@ -102,12 +106,13 @@ struct CombineArgs {
 // stream packets).
 hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                               hipEvent_t ev_stop);
+// the fp8-family kernel serves both quantised formats (fp4: the e2m1 row)
 hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                             hipEvent_t ev_stop);
+                             hipEvent_t ev_stop, bool fp4 = false);
 hipError_t launch_decode_bf16_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                                      hipEvent_t ev_stop);
 hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                                    hipEvent_t ev_stop);
+                                    hipEvent_t ev_stop, bool fp4 = false);
 hipError_t launch_sparse_rows(const SparseRowsArgs& a, hipStream_t stream);
 // max_splits: an upper bound on the splits of one sequence (the worker
 // count); it sizes the combine's LDS and picks its shape.

@@ -12,7 +12,10 @@ import torch
 from mla_inputs import make_workload, to_torch, Workload
 from oracle import mla_decode_ref
 
-TOL = {"bf16": 2e-2, "fp8": 4e-2}     # max|err| <= TOL * RMS(out), the stated bound
+# max|err| <= TOL * RMS(out): the stated bounds (bf16 2e-2, quantised fp8
+# cache 4e-2); the fp4 cache, decoded from identical bytes by the oracle,
+# is held to the fp8 bound
+TOL = {"bf16": 2e-2, "fp8": 4e-2, "fp4": 4e-2}
 
 
 def say(msg: str) -> None:

@@ -47,6 +47,10 @@ def test_row_sizes():
     # the 512-dimension FP8 row of the DeepSeek-R1 record, constraint (2)
     assert mla.kv_row_bytes("fp8", 448, 64) == 528
     assert mla.kv_row_stride("fp8", 448, 64) == 528
+    # its fp4 variant: 288 bytes at 512 dimensions; 324 (stride 336) at 576
+    assert mla.kv_row_bytes("fp4", 448, 64) == 288
+    assert mla.kv_row_bytes("fp4") == 324
+    assert mla.kv_row_stride("fp4") == 336
     lib = _lib()
     assert lib.mla_kv_row_bytes(7, 512, 64) == 0
     assert lib.mla_kv_row_bytes(1, 500, 64) == 0        # not a multiple of 32
@@ -84,6 +88,7 @@ def _init(**over):
     (dict(block_size=0), 1),
     (dict(max_blocks_per_seq=0), 1),
     (dict(kv_dtype=5), 1),
+    (dict(kv_dtype=3), 1),
     (dict(softmax_scale=0.0), 1),
     (dict(softmax_scale=float("nan")), 1),
     (dict(softmax_scale=-1.0), 1),

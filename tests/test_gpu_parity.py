@@ -14,7 +14,8 @@ from gpu_helpers import run_gpu, oracle, assert_parity, make_decoder, say
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["single_1k_small", "paged_b32_small", "long_ctx_b4_small", "fp8_b64_small", "mtp2_b128_small"]
+SMALL = ["single_1k_small", "paged_b32_small", "long_ctx_b4_small", "fp8_b64_small", "mtp2_b128_small",
+         "fp4_b64_small"]
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -41,6 +42,7 @@ FULL_SAMPLES = {
     "long_ctx_b4": [0, 2],
     "fp8_b64": [0, 33, 63],
     "mtp2_b128": [0, 64, 127],
+    "fp4_b64": [0, 33, 63],
 }
 
 
@@ -99,9 +101,12 @@ def _repage(w, page: int, seed: int):
     pool = np.empty((pool_pages, page) + w.pool.shape[2:], dtype=w.pool.dtype)
     if s.kv_dtype == "bf16":
         pool[...] = 0x7FC0
-    else:
+    elif s.kv_dtype == "fp8":
         pool[...] = 0xFF
         pool[..., :s.d] = 0x7F
+    else:
+        pool[...] = 0xFF
+        pool[..., :s.d // 2] = 0x77
     bt = np.full((s.batch, max(int(nb.max()), 1)), -1, dtype=np.int32)
     off = 0
     for b in range(s.batch):
@@ -116,7 +121,8 @@ def _repage(w, page: int, seed: int):
     return dataclasses.replace(w, spec=spec, pool=pool, block_table=bt)
 
 
-@pytest.mark.parametrize("name", ["paged_b32_small", "fp8_b64_small", "mtp2_b128_small", "long_ctx_b4_small"])
+@pytest.mark.parametrize("name", ["paged_b32_small", "fp8_b64_small", "mtp2_b128_small", "long_ctx_b4_small",
+                                  "fp4_b64_small"])
 @pytest.mark.parametrize("page", [16, 32, 128, 256])
 def test_page_block_sizes(name, page):
     # page blocks other than 64 ("DeepSeek-R1" record, constraint (1): 32 for
@@ -154,7 +160,7 @@ def test_repeat_runs_bitwise_identical(name):
     np.testing.assert_array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("name", ["paged_b32_small", "fp8_b64_small"])
+@pytest.mark.parametrize("name", ["paged_b32_small", "fp8_b64_small", "fp4_b64_small"])
 def test_unread_bytes_do_not_matter(name):
     # rewrite every byte the decode must not read (tails, spare pages, padding)
     w = make_workload(name)
@@ -167,6 +173,8 @@ def test_unread_bytes_do_not_matter(name):
     pool2[~used] = 0x5A5A if w.spec.kv_dtype == "bf16" else 0xFF
     if w.spec.kv_dtype == "fp8":
         pool2[:, :, 594:] = 0x7F
+    if w.spec.kv_dtype == "fp4":
+        pool2[:, :, 324:] = 0x7F                      # row padding
     w2 = dataclasses.replace(w, pool=pool2)
     o1, l1 = run_gpu(w, num_workers=5)
     o2, l2 = run_gpu(w2, num_workers=5)
@@ -192,6 +200,10 @@ EDGE = [
     WorkloadSpec("edge_flat_q0_fp8", 5, ("fixed", (1, 36, 100, 700, 1500)), q_scale=0.0, kv_dtype="fp8",
                  spare_pages=4, seed=20),
     WorkloadSpec("edge_flat_mtp", 4, ("fixed", (2, 37, 101, 701)), q_scale=0.02, s_q=2, spare_pages=4, seed=24),
+    WorkloadSpec("edge_fp4", 4, ("fixed", (1, 63, 64, 700)), kv_dtype="fp4", spare_pages=4, seed=25,
+                 outlier_p=0.01, outlier_mult=20.0),
+    WorkloadSpec("edge_flat_q0_fp4", 5, ("fixed", (1, 36, 100, 700, 1500)), q_scale=0.0, kv_dtype="fp4",
+                 spare_pages=4, seed=26),
 ]
 
 

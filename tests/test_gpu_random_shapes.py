@@ -22,8 +22,8 @@ N_CASES = 24
 
 def _case(seed: int):
     rng = np.random.default_rng(1000 + seed)
-    kv = "fp8" if seed % 2 else "bf16"
-    sparse = seed % 4 >= 2
+    kv = ("bf16", "fp8", "bf16", "fp4")[seed % 4]
+    sparse = seed % 8 >= 4
     page = int(rng.choice([16, 32, 64, 64, 128, 256]))
     s_q = int(rng.choice([1, 1, 2, 3, 4]))
     n_h = int(rng.choice([32, 64, 128, 128, 256]))
@@ -38,7 +38,7 @@ def _case(seed: int):
     workers = int(rng.choice([0, 0, 1, 5, 37, 300]))
     spec = WorkloadSpec(f"rand{seed}", batch, ("fixed", lens), kv_dtype=kv, s_q=s_q, n_h=n_h, page=page,
                         q_scale=q_scale, spare_pages=3, topk=topk, seed=2000 + seed,
-                        outlier_p=0.01 if kv == "fp8" else 0.0, outlier_mult=20.0)
+                        outlier_p=0.01 if kv != "bf16" else 0.0, outlier_mult=20.0)
     return spec, workers
 
 

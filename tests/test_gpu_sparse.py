@@ -49,6 +49,7 @@ VARIANTS = [
     SPECS["sparse_fp8_topk2048_b64_small"],
     dataclasses.replace(SPECS["sparse_fp8_topk2048_b64_small"], name="sparse_fp8_mtp2_small", s_q=2, seed=50),
     dataclasses.replace(SPECS["sparse_fp8_topk2048_b64_small"], name="sparse_fp8_page32_small", page=32, seed=51),
+    dataclasses.replace(SPECS["sparse_fp8_topk2048_b64_small"], name="sparse_fp4_small", kv_dtype="fp4", seed=54),
     # flat softmax: a token wrongly counted or dropped by the tile mask moves
     # the output by about 1/n (the lists here are shorter than 64 tokens past
     # the last full tile, both tile halves partly valid)
@@ -112,7 +113,7 @@ def test_sparse_reads_only_selected_rows(kv_dtype):
     np.testing.assert_array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "fp4"])
 def test_sparse_over_whole_context_equals_dense_bitwise(kv_dtype):
     # index lists 0 .. L-1 in order (padded with -1) visit the dense decode's
     # tiles in the dense order; with one worker neither run splits, so the
