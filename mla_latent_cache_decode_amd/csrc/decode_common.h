@@ -177,7 +177,54 @@ __device__ __forceinline__ int plan_len(const DecodeArgs& a, int b) {
 // records, for every sequence whose cost position lies in this worker's
 // quota, the number of segments it is split into and its first partial slot
 // (read by the combine); only the first row group does that.
+// The same plan for a batch of at most 64 sequences: one wave holds every
+// length, so each wave forms the whole plan with wave-level scans on its
+// own -- no workgroup barrier and no LDS (the planner sits at the head of
+// every workgroup's critical path).  Wave 0 of the first row group writes
+// the per-sequence records.
+__device__ WorkerStart plan_worker_wave(const DecodeArgs& a, int worker, bool write_info, int tid) {
+    const int B = a.batch, G = a.num_workers, c = a.overhead_units;
+    const int lane = tid & 63;
+    const int L = lane < B ? plan_len(a, lane) : 0;
+    const int pages = L > 0 ? (L + kPage - 1) / kPage : 0;
+    const int cost_in = pages > 0 ? pages + c : 0;
+    const int cost_incl = wave_incl_scan(cost_in, lane);
+    // results are wave-uniform: readfirstlane keeps them in SGPRs for the
+    // segment loop (as VGPRs they would crowd the tile loop's registers)
+    const int total = __builtin_amdgcn_readfirstlane(__shfl(cost_incl, 63));
+    const int64_t Q = max(max(((int64_t)total + G - 1) / G, (int64_t)a.min_quota), (int64_t)1);
+    const int64_t w_lo = (int64_t)worker * Q;
+    const int64_t C = cost_incl - cost_in;                  // where sequence `lane` starts
+    const int64_t A = C + c, E = A + pages;
+    const int n = pages > 0 ? (int)((E - 1) / Q - A / Q + 1) : 0;
+    const int slot_in = n > 1 ? n : 0;
+    const int slot = wave_incl_scan(slot_in, lane) - slot_in;
+    if (write_info && tid < 64 && lane < B) {
+        const int64_t owner = pages > 0 ? A / Q : min(C / Q, (int64_t)G - 1);
+        if (owner == worker) {
+            a.plan.seq_nsplit[lane] = n;
+            a.plan.seq_slot[lane] = slot;
+        }
+    }
+    // the first sequence whose pages reach past w_lo
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(lane < B && pages > 0 && E > w_lo);
+    WorkerStart ws;
+    ws.quota = Q;
+    if (m) {
+        const int first = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(m));
+        ws.b = first;
+        ws.cost = __builtin_amdgcn_readfirstlane(__shfl((int)C, first));   // C < 2^31 for 64 sequences
+        ws.slot = __builtin_amdgcn_readfirstlane(__shfl(slot, first));
+    } else {
+        ws.b = B;
+        ws.cost = 0;
+        ws.slot = 0;
+    }
+    return ws;
+}
+
 __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_info, int* sbuf, int tid) {
+    if (a.batch <= 64) return plan_worker_wave(a, worker, write_info, tid);
     const int B = a.batch, G = a.num_workers, c = a.overhead_units;
     int t_cost = 0;
     const int my_len = tid < B ? plan_len(a, tid) : 0;      // reused by the first chunk
