@@ -115,11 +115,16 @@ __device__ __forceinline__ bool raise_max(float mx, RowState& rs) {
 // kSparse: the top-k decode ("DeepSeek-V3.2" record).  A unit (one query
 // position of one sequence, n_h rows) attends to the topk rows its index
 // list selects; tile p holds entries 64p .. 64p + 63, gathered row by row
-// through the pre-pass's row table (wave w loads tokens 16w .. 16w + 15),
-// and the pre-pass's tile mask takes the place of the length mask.
-// Entries that do not take part are fetched from a row of zeros that the
-// pre-pass writes into the workspace (their weights are 0; zeros keep
-// 0 x V finite).
+// (wave w loads tokens 16w .. 16w + 15).  The kernel turns the list into
+// rows itself, in its page pipeline: the entries of tile p + 3 are loaded
+// during tile p; those of tile p + 2 become the tile's mask (a ballot of
+// 0 <= t < the query's causal context) and, for each lane's two tokens,
+// block-table loads; tile p + 1's rows (page * block + slot) feed its
+// gathers.  The mask takes the place of the length mask.  Entries that do
+// not take part are fetched from a row of zeros (their weights are 0;
+// zeros keep 0 x V finite).
+__device__ __attribute__((aligned(256))) uint8_t g_sparse_zero_row[kSparseZeroRowBytes] = {};
+
 template <int PS, bool kSparse>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
     typedef PageGeom<kSparse ? 16 : PS> Geom;
@@ -216,24 +221,51 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             }
         };
 
-        // sparse gather: the row-id pair of this lane's two tokens (16w + x
-        // and 16w + 8 + x, x = lane >> 3 of a piece) and the tile mask, by
-        // vector loads two tiles ahead; tiles at or past p_hi read zeros and
-        // are never used
-        const int64_t tiles_u = kSparse ? (L + kPage - 1) / kPage : 0;
-        const __amdgpu_buffer_rsrc_t r_rows =
-            make_rsrc((const uint8_t*)(a.sparse_rows + (kSparse ? (int64_t)b * tiles_u * 64 : 0)), p_hi * 256);
-        const __amdgpu_buffer_rsrc_t r_mask =
-            make_rsrc((const uint8_t*)(a.sparse_masks + (kSparse ? (int64_t)b * tiles_u : 0)), p_hi * 8);
-        auto load_rows = [&](int p) -> u32x2 {
-            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                 r_rows, p * 256 + (wave * 8 + (pinned(lane0) >> 3)) * 8, 0, 0));
+        // sparse gather plan.  Unit b is query position j of sequence b_seq;
+        // its entries read through r_idx (entry k of the list at 4k), the
+        // block table of b_seq through r_bt.
+        const int sq = kSparse ? a.sparse_sq : 1;
+        const int b_seq = kSparse ? b / sq : b;
+        const int n_ctx = kSparse ? ld_const(a.seq_lens + b_seq) - sq + 1 + (b - b_seq * sq) : 0;
+        const __amdgpu_buffer_rsrc_t r_idx =
+            make_rsrc((const uint8_t*)(a.sparse_indices + (kSparse ? (int64_t)b * L : 0)), kSparse ? L * 4 : 0);
+        const __amdgpu_buffer_rsrc_t r_bt =
+            make_rsrc((const uint8_t*)(a.block_table + (int64_t)b_seq * a.max_blocks), kSparse ? a.max_blocks * 4 : 0);
+        const int pshift = __builtin_ctz((unsigned)a.page_size);
+        // entry 64p + lane of the list (entries past topk are masked below)
+        auto load_idx = [&](int p) -> int {
+            return __builtin_amdgcn_raw_buffer_load_b32(r_idx, (p * kPage + pinned(lane0)) * 4, 0, 0);
         };
-        auto load_mask = [&](int p) -> u32x2 {
-            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r_mask, p * 8, 0, 0));
+        // tile p's mask (bit t: entry 64p + t is a token of the query's
+        // context) and, for this lane's two tokens 16w + x and 16w + 8 + x
+        // (x = lane >> 3 of a piece), their block-table entries in flight and
+        // their slots in the page (0xFFFF: no token)
+        struct SparsePend {
+            uint32_t e0, e1, slots;
+        };
+        auto expand = [&](int iv, int p, uint32_t& m_lo, uint32_t& m_hi) -> SparsePend {
+            const int l = pinned(lane0);
+            const bool valid = p < p_hi && p * kPage + l < L && iv >= 0 && iv < n_ctx;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(valid);
+            m_lo = (uint32_t)m;
+            m_hi = (uint32_t)(m >> 32);
+            const int s0 = wave * 16 + (l >> 3), s1 = s0 + 8;
+            const int t0 = __shfl(iv, s0), t1 = __shfl(iv, s1);
+            const bool v0 = (m >> s0) & 1, v1 = (m >> s1) & 1;
+            SparsePend r;
+            r.e0 = __builtin_amdgcn_raw_buffer_load_b32(r_bt, (v0 ? t0 >> pshift : 0) * 4, 0, 0);
+            r.e1 = __builtin_amdgcn_raw_buffer_load_b32(r_bt, (v1 ? t1 >> pshift : 0) * 4, 0, 0);
+            r.slots = (v0 ? (uint32_t)(t0 & (a.page_size - 1)) : 0xFFFFu) |
+                      ((v1 ? (uint32_t)(t1 & (a.page_size - 1)) : 0xFFFFu) << 16);
+            return r;
+        };
+        // the two tokens' cache rows (page * block + slot), kNoRow for none
+        auto rows_of = [&](const SparsePend& q) -> u32x2 {
+            const uint32_t s0 = q.slots & 0xFFFFu, s1 = q.slots >> 16;
+            return u32x2{s0 == 0xFFFFu ? kNoRow : (q.e0 << pshift) + s0, s1 == 0xFFFFu ? kNoRow : (q.e1 << pshift) + s1};
         };
         // what entries that do not take part fetch: a row of zeros
-        const uint8_t* const zero_row = a.sparse_zero_row;
+        const uint8_t* const zero_row = g_sparse_zero_row;
         // piece k of tile p (row ids rw): token 16w + 8(k & 1) + x, column
         // block k >> 1, landing at LDS piece (k >> 1) * 8 + 2w + (k & 1)
         auto dma_sparse = [&](const u32x2& rw, int p, LDS_AS uint8_t* tile, auto k_c) {
@@ -254,14 +286,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
         // they are in flight (loads complete in order, so waiting for the
         // entry does not wait for the queries), then the first page
         int phys0 = 0, phys_next = 0, rows0 = 0;
-        u32x2 rw0, rw_next, mk0, mk1;
         uint32_t mk_lo = ~0u, mk_hi = ~0u;       // sparse: mask of the current tile
         uint32_t mk_next_lo = ~0u, mk_next_hi = ~0u;
+        SparsePend pend0, pend;                  // sparse: tiles p_lo and p_lo + 1, then p + 1
+        int iv = 0;                              // sparse: the lane's entry of tile p + 2
         if constexpr (kSparse) {
-            rw0 = load_rows(p_lo);
-            mk0 = load_mask(p_lo);
-            rw_next = load_rows(p_lo + 1);
-            mk1 = load_mask(p_lo + 1);
+            const int iv0 = load_idx(p_lo), iv1 = load_idx(p_lo + 1);
+            iv = load_idx(p_lo + 2);
+            pend0 = expand(iv0, p_lo, mk_lo, mk_hi);
+            pend = expand(iv1, p_lo + 1, mk_next_lo, mk_next_hi);
         } else {
             phys0 = load_phys(p_lo);
             phys_next = load_phys(p_lo + 1);
@@ -282,11 +315,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8*)(qrow + ks * 16);
         }
         if constexpr (kSparse) {
+            const u32x2 rw0 = rows_of(pend0);
             static_for<0, kDmaPerWave>([&](auto k) { dma_sparse(rw0, p_lo, tiles[0], k); });
-            mk_lo = __builtin_amdgcn_readfirstlane(mk0[0]);
-            mk_hi = __builtin_amdgcn_readfirstlane(mk0[1]);
-            mk_next_lo = __builtin_amdgcn_readfirstlane(mk1[0]);
-            mk_next_hi = __builtin_amdgcn_readfirstlane(mk1[1]);
         } else {
             const __amdgpu_buffer_rsrc_t r0 = rsrc_of(p_lo, phys0, rows0);
 #pragma unroll
@@ -307,10 +337,14 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             LDS_AS uint8_t* const tnext = tiles[(p - p_lo + 1) & 1];
             __amdgpu_buffer_rsrc_t r_next;
             int phys_after = 0;
-            u32x2 rw_after, mk_after;
+            u32x2 rw_next;
+            uint32_t mk_after_lo = ~0u, mk_after_hi = ~0u;
             if constexpr (kSparse) {
-                rw_after = load_rows(p + 2);
-                mk_after = load_mask(p + 2);
+                // tile p + 1's rows (its block-table entries landed during
+                // tile p - 1), tile p + 2's mask and entries, tile p + 3's list
+                rw_next = rows_of(pend);
+                pend = expand(iv, p + 2, mk_after_lo, mk_after_hi);
+                iv = load_idx(p + 3);
             } else {
                 r_next = page_rsrc(p + 1, phys_next);
                 phys_after = load_phys(p + 2);
@@ -535,11 +569,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
                 for (int hb = 0; hb < 4; ++hb) asm volatile("" : "+a"(o[db][hb]));
             rs.l += lsum;
             if constexpr (kSparse) {
-                rw_next = rw_after;
                 mk_lo = mk_next_lo;
                 mk_hi = mk_next_hi;
-                mk_next_lo = __builtin_amdgcn_readfirstlane(mk_after[0]);
-                mk_next_hi = __builtin_amdgcn_readfirstlane(mk_after[1]);
+                mk_next_lo = mk_after_lo;
+                mk_next_hi = mk_after_hi;
             } else {
                 phys_next = phys_after;
             }

@@ -68,6 +68,9 @@ struct DecodeArgs {
     const uint32_t* sparse_rows;   // [units][tiles][32 pairs]: see SparseRowsArgs
     const uint64_t* sparse_masks;  // [units][tiles]: bit t = token t of the tile takes part
     const uint8_t* sparse_zero_row; // kSparseZeroRowBytes of zeros: what entries that do not take part fetch
+    // the bf16 sparse decode reads the index lists itself (no pre-pass):
+    const int32_t* sparse_indices;  // [units][topk] token positions
+    int32_t sparse_sq;              // query positions per sequence (unit u = b * sparse_sq + j)
 };
 
 // Pre-pass of the sparse decode: turns each unit's index list into physical
