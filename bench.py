@@ -8,7 +8,7 @@ workload: batch 4, seq_lens
 (block 64, permuted pages).  Inputs are seeded synthetic data already
 resident in HBM before the timed region.  ``--workload`` picks another
 recipe (a parity workload, or the sparse top-k one, whose step is the
-row-table pre-pass, the gathering decode and the combine).
+gathering decode, which reads the index lists itself, and the combine).
 
 Prints one JSON line: KV-read GB/s (whole job), TFLOP/s, the dominant
 kernel's roofline (decode kernel: algorithmic KV bytes per launch over its

@@ -149,11 +149,8 @@ mla_status_t mla_decode_run(mla_decode_handle_t h,
  * mla_decode_sparse_run needs for `batch` sequences (0 <= batch <= max_batch)
  * and index lists of `topk` entries (1 <= topk <= 2^20).  `bytes` is a host
  * pointer.  The workspace holds the work plan and split partials of
- * batch * s_q query units and, for the fp8 and fp4 caches, the gather table
- * of their pre-pass: one 4-byte row id per index entry (rounded up to 64 per
- * unit) and one 8-byte mask per 64 entries (and a 2 KiB row of zeros that
- * entries which do not take part are fetched from).  With a bf16 cache the
- * size does not depend on topk. */
+ * batch * s_q query units; its size does not depend on topk (the decode
+ * reads the index lists itself, nothing per entry is stored). */
 mla_status_t mla_decode_sparse_workspace_size(mla_decode_handle_t h, int32_t batch, int32_t topk,
                                               size_t* bytes);
 
@@ -173,13 +170,10 @@ mla_status_t mla_decode_sparse_workspace_size(mla_decode_handle_t h, int32_t bat
  *   every other argument as for mla_decode_run (the handle's s_q, n_h,
  *   block_size and softmax scale apply); workspace >=
  *   mla_decode_sparse_workspace_size(batch, topk) bytes.
- * Every cache format is served.  With a bf16 cache two kernels are enqueued
- * on the stream: the decode, which reads the index lists and the block
- * table itself and gathers the rows, and the split combine.  The fp8 and
- * fp4 caches add a pre-pass before the decode that turns the lists into
- * physical row ids (through the block table) and masks.  Only the listed
- * rows are read; the block-table entries of listed valid tokens must be
- * valid pages. */
+ * Every cache format is served.  Two kernels are enqueued on the stream:
+ * the decode, which reads the index lists and the block table itself and
+ * gathers the rows, and the split combine.  Only the listed rows are read;
+ * the block-table entries of listed valid tokens must be valid pages. */
 mla_status_t mla_decode_sparse_run(mla_decode_handle_t h,
                                    const void* q,
                                    const void* kv_pages,

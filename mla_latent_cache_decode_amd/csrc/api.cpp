@@ -58,10 +58,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int32_t kMaxTopk = 1 << 20;
 
 // Workspace of a sparse run: the plan and partials of batch * s_q units of
-// n_h rows and, for the quantised caches, the row table and the tile masks
-// of the pre-pass (the bf16 decode reads the index lists itself).
+// n_h rows.
 struct SparseLayout {
-    size_t seq_nsplit, seq_slot, part_lse, part_o, rows, masks, zero_row, total;
+    size_t seq_nsplit, seq_slot, part_lse, part_o, total;
     int units, tiles, row_groups, workers, slots;
 };
 
@@ -85,11 +84,6 @@ SparseLayout sparse_layout(const mla_decode_handle* h, int32_t batch, int32_t to
     l.seq_slot = off;    off += align_up(nu * sizeof(int32_t));
     l.part_lse = off;    off += align_up((size_t)l.slots * h->p.n_h * sizeof(float));
     l.part_o = off;      off += align_up((size_t)l.slots * h->p.n_h * mla::kDc * sizeof(uint16_t));
-    if (h->p.kv_dtype != MLA_KV_BF16) {
-        l.rows = off;        off += align_up(nu * l.tiles * mla::kPage * sizeof(uint32_t));
-        l.masks = off;       off += align_up(nu * l.tiles * sizeof(uint64_t));
-        l.zero_row = off;    off += align_up(mla::kSparseZeroRowBytes);
-    }
     l.total = off;
     return l;
 }
@@ -124,9 +118,6 @@ mla::DecodeArgs decode_args(const mla_decode_handle* h, const void* q, const voi
     da.min_quota = kMinQuota;
     da.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
     da.sparse_topk = 0;
-    da.sparse_rows = nullptr;
-    da.sparse_masks = nullptr;
-    da.sparse_zero_row = nullptr;
     da.sparse_indices = nullptr;
     da.sparse_sq = 1;
     return da;
@@ -328,40 +319,17 @@ mla_status_t mla_decode_sparse_run(mla_decode_handle_t h, const void* q, const v
     plan.slots = l.slots;
     plan.part_o = (uint16_t*)(ws + l.part_o);
     hipStream_t stream = (hipStream_t)hip_stream;
-    const bool bf16 = h->p.kv_dtype == MLA_KV_BF16;
-
-    mla::SparseRowsArgs ra{};
-    ra.indices = indices;
-    ra.block_table = block_table;
-    ra.seq_lens = seq_lens;
-    ra.rows = (uint32_t*)(ws + l.rows);
-    ra.masks = (uint64_t*)(ws + l.masks);
-    ra.zero_row = ws + l.zero_row;
-    ra.units = l.units;
-    ra.s_q = h->p.s_q;
-    ra.topk = topk;
-    ra.tiles = l.tiles;
-    ra.max_blocks = h->p.max_blocks_per_seq;
-    ra.page_size = h->p.block_size;
-    if (!bf16 && mla::launch_sparse_rows(ra, stream) != hipSuccess) return MLA_ERR_HIP;
-
     // every (sequence, query position) is a unit of n_h rows attending to its own tokens
     mla::DecodeArgs da = decode_args(h, q, kv_pages, block_table, seq_lens, out, lse, plan);
     da.batch = l.units;
     da.s_q = 1;
     da.num_workers = l.workers;
     da.sparse_topk = topk;
-    if (bf16) {
-        da.sparse_indices = indices;
-        da.sparse_sq = h->p.s_q;
-    } else {
-        da.sparse_rows = ra.rows;
-        da.sparse_masks = ra.masks;
-        da.sparse_zero_row = ra.zero_row;
-    }
+    da.sparse_indices = indices;
+    da.sparse_sq = h->p.s_q;
     const hipEvent_t e0 = h->ev_start && h->ev_stop ? h->ev_start : nullptr;
     const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
-    const hipError_t e = bf16
+    const hipError_t e = h->p.kv_dtype == MLA_KV_BF16
                              ? mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1)
                              : mla::launch_decode_fp8_sparse(da, l.row_groups, stream, e0, e1,
                                                              h->p.kv_dtype == MLA_KV_FP4_E2M1_E8M0);

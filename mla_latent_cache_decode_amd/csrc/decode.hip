@@ -207,7 +207,7 @@ struct WaveState {
 // pv_hook(step) inside P.V step `step` (both compile-time); they carry the
 // page pipeline's loads and LDS stores so that these issue between MFMAs.
 // Tokens of the tile that take part: the first n_valid (dense), or the set
-// bits of `mask` (sparse: the pre-pass's tile mask).
+// bits of `mask` (sparse: the tile's mask; bit t = token t).
 template <bool kSparse, typename QkHook, typename PvHook>
 __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f16x8 (&qf)[kQRegSteps],
                                              const LDS_AS uint8_t* qr, WaveState& st, int n_valid, uint64_t mask,
@@ -361,10 +361,17 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
 // the decode kernel
 // ---------------------------------------------------------------------------
 // kSparse: the top-k decode ("DeepSeek-V3.2" record): a unit (one query
-// position, n_h rows) attends to the rows its index list selects; each lane
-// gathers its token's row through the pre-pass's row table (entries that
-// do not take part read the workspace's zero row) and the pre-pass's tile
-// mask takes the place of the length mask.
+// position, n_h rows) attends to the rows its index list selects, 64
+// entries a tile.  Lane l loads entry l of the tile; a ballot of its
+// validity (0 <= t < the query's causal context) gives the mask that takes
+// the place of the length mask, and lane l of wave w gathers the row of
+// entry 16w + (l & 15), moved to it by two lane swaps (entries that do not
+// take part read a row of zeros).  The list is turned into rows in the
+// page pipeline: during tile p the entries of tile p + 4 are loaded and
+// those of tile p + 3 (loaded a tile earlier) issue their block-table
+// loads, whose results give tile p + 3's rows one tile later.
+__device__ __attribute__((aligned(256))) uint8_t g_sparse_zero_row[kSparseZeroRowBytes] = {};
+
 template <int PS, bool kSparse, bool kFp4>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArgs a) {
     typedef std::conditional_t<kFp4, Fp4Pieces, Fp8Pieces> Pieces;
@@ -427,30 +434,57 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         // The entry read for tile p is that of the page holding token tok0
         // of the tile (the wave's page); an entry past the sequence's last
         // page may be read but is not used (its rows are past n_load).
-        const __amdgpu_buffer_rsrc_t bt = make_rsrc((const uint8_t*)(a.block_table + (int64_t)b * a.max_blocks),
-                                                    (PS < kPage ? min(Geom::entries(p_hi), a.max_blocks)
-                                                                : Geom::entries(p_hi)) * 4);
-        // sparse: row table and tile masks of this unit (tiles at or past
-        // p_hi read zeros and are not used)
-        const int64_t tiles_u = kSparse ? pages : 0;
-        const __amdgpu_buffer_rsrc_t r_rows =
-            make_rsrc((const uint8_t*)(a.sparse_rows + (kSparse ? (int64_t)b * tiles_u * 64 : 0)), p_hi * 256);
-        const __amdgpu_buffer_rsrc_t r_mask =
-            make_rsrc((const uint8_t*)(a.sparse_masks + (kSparse ? (int64_t)b * tiles_u : 0)), p_hi * 8);
-        // dense: the block-table entry of tile p's page for this wave;
-        // sparse: the row id of this lane's token of tile p (token 16w + (i & 15)
-        // sits in the table's pair (w * 8 + (i & 7)), element (i >> 3) & 1)
+        // sparse: unit b is query position j of sequence b_seq, whose block
+        // table bt covers; its causal context is n_ctx tokens
+        const int sq = kSparse ? a.sparse_sq : 1;
+        const int b_seq = b / sq;
+        const int n_ctx = kSparse ? ld_const(a.seq_lens + b_seq) - sq + 1 + (b - b_seq * sq) : 0;
+        const __amdgpu_buffer_rsrc_t bt =
+            kSparse ? make_rsrc((const uint8_t*)(a.block_table + (int64_t)b_seq * a.max_blocks), a.max_blocks * 4)
+                    : make_rsrc((const uint8_t*)(a.block_table + (int64_t)b * a.max_blocks),
+                                (PS < kPage ? min(Geom::entries(p_hi), a.max_blocks) : Geom::entries(p_hi)) * 4);
+        // dense: the block-table entry of tile p's page for this wave
         auto load_phys = [&](int p) -> int {
-            if constexpr (kSparse) {
-                const int l = pinned(tid & 63);
-                return __builtin_amdgcn_raw_buffer_load_b32(
-                    r_rows, p * 256 + ((wave * 8 + (l & 7)) * 2 + ((l >> 3) & 1)) * 4, 0, 0);
-            } else {
-                return __builtin_amdgcn_raw_buffer_load_b32(bt, Geom::entry(p, tok0) * 4, 0, 0);
-            }
+            return __builtin_amdgcn_raw_buffer_load_b32(bt, Geom::entry(p, tok0) * 4, 0, 0);
         };
-        auto load_mask = [&](int p) -> u32x2 {
-            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r_mask, p * 8, 0, 0));
+        // sparse: entry l of tile p's list for lane l (entries past topk
+        // read 0 and are masked)
+        const __amdgpu_buffer_rsrc_t r_idx =
+            make_rsrc((const uint8_t*)(a.sparse_indices + (kSparse ? (int64_t)b * L : 0)), kSparse ? L * 4 : 0);
+        const int e_tok = wave * 16 + (tid & 15);
+        const int pshift = __builtin_ctz((unsigned)a.page_size);
+        auto load_idx = [&](int p) -> int {
+            return __builtin_amdgcn_raw_buffer_load_b32(r_idx, (p * kPage + pinned(tid & 63)) * 4, 0, 0);
+        };
+        auto takes_part = [&](int p, int e, int t) { return p < p_hi && p * kPage + e < L && t >= 0 && t < n_ctx; };
+        // x of lane 16 * wave + (l & 15), for every lane l: permlane16_swap
+        // of x with itself yields rows (0, 0, 2, 2) and (1, 1, 3, 3) of x,
+        // permlane32_swap of a value with itself its lower and its upper half
+        // in both halves
+        auto quarter_bcast = [&](int x) -> int {
+            const auto r16 = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+            const unsigned y = (wave & 1) ? r16[1] : r16[0];
+            const auto r32 = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+            return (int)((wave & 2) ? r32[1] : r32[0]);
+        };
+        // sparse: tile p's entries (lane l: entry l) -> the tile's mask, and
+        // the lane's token's block-table entry in flight and its slot in the
+        // page (-1: no token)
+        struct SparsePend {
+            int e, slot;
+        };
+        auto expand = [&](int p, int iv, uint64_t& mask) -> SparsePend {
+            mask = __builtin_amdgcn_ballot_w64(takes_part(p, tid & 63, iv));
+            const int t = quarter_bcast(iv);
+            const bool v = takes_part(p, e_tok, t);
+            SparsePend r;
+            r.e = __builtin_amdgcn_raw_buffer_load_b32(bt, (v ? t >> pshift : 0) * 4, 0, 0);
+            r.slot = v ? t & (a.page_size - 1) : -1;
+            return r;
+        };
+        // sparse: the row id (page * block + slot) of a landed entry
+        auto row_of = [&](const SparsePend& q) -> int {
+            return q.slot < 0 ? (int)kNoRow : (q.e << pshift) + q.slot;
         };
         // dense: descriptor over the rows of tile p in the wave's page
         // (physical page phys) that the workgroup loads, size 0 past p_hi;
@@ -458,7 +492,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         auto page_rsrc = [&](int p, int phys) {
             if constexpr (kSparse) {
                 const bool live = p < p_hi && (uint32_t)phys != kNoRow;
-                return live ? a.kv + (uint64_t)(uint32_t)phys * kRowBytes : a.sparse_zero_row;
+                return live ? a.kv + (uint64_t)(uint32_t)phys * kRowBytes : (const uint8_t*)g_sparse_zero_row;
             } else {
                 const int nv = p < p_hi ? min(max(n_load - p * kPage - tok0, 0), Geom::kRangeTok) : 0;
                 return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes +
@@ -467,13 +501,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
             }
         };
         typedef decltype(page_rsrc(0, 0)) Src;
-        // a tile mask loaded as two words, made wave-uniform (each word
-        // through uint32: readfirstlane's int would sign-extend into the
-        // upper word)
-        auto join_mask = [](const u32x2& v) -> uint64_t {
-            return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(v[1]) << 32) |
-                   (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(v[0]);
-        };
 
         // this wave's 32 query rows as MFMA B operands (q_abs || q_R): bf16
         // loaded, scaled per head by 2^-sh so the head's max |q| lands in
@@ -487,8 +514,23 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         // entries, then the first page as soon as its entry lands, then the
         // queries; the page is stored while the queries are still arriving
         // (loads complete in issue order), and the queries are converted after
-        const int phys0 = load_phys(p_lo);
-        const int phys1 = load_phys(p_lo + 1);
+        int phys0, phys1;
+        SparsePend pend;        // sparse: tile p + 2's rows in flight (tile p_lo + 2 in the prologue)
+        int iv_next = 0;        // sparse: the lane's entry of tile p + 3
+        // sparse: masks of tiles p .. p + 3 (wave-uniform)
+        uint64_t mask_cur = ~0ull, mask1 = 0, mask2 = 0, mask3 = 0;
+        if constexpr (kSparse) {
+            const int iv0 = load_idx(p_lo), iv1 = load_idx(p_lo + 1), iv2 = load_idx(p_lo + 2);
+            iv_next = load_idx(p_lo + 3);
+            const SparsePend pend0 = expand(p_lo, iv0, mask_cur);
+            const SparsePend pend1 = expand(p_lo + 1, iv1, mask1);
+            pend = expand(p_lo + 2, iv2, mask2);
+            phys0 = row_of(pend0);
+            phys1 = row_of(pend1);
+        } else {
+            phys0 = load_phys(p_lo);
+            phys1 = load_phys(p_lo + 1);
+        }
 
         // scale each head's query by 2^-sh so its max |q| lands in [2^14, 2^15)
         // and convert to fp16 (exact up to fp16 subnormals); the q_R part
@@ -555,14 +597,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
             for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = __builtin_bit_cast(f16x8, *(const bf16x8*)(qrow + ks * 16));
         }
         Src r_next = page_rsrc(p_lo + 1, phys1);
-        int phys2 = load_phys(p_lo + 2);
-        // sparse: masks of the current and the next tile (loaded two ahead)
-        uint64_t mask_cur = ~0ull, mask_next = ~0ull;
-        u32x2 mkv0, mkv1;
-        if constexpr (kSparse) {
-            mkv0 = load_mask(p_lo);
-            mkv1 = load_mask(p_lo + 1);
-        }
+        int phys2 = kSparse ? 0 : load_phys(p_lo + 2);
         st.m = -__builtin_inff();
         st.l = 0.f;
         st.o_zero = true;
@@ -573,19 +608,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
             if constexpr (k < Pieces::first(1)) pc.issue(stg[k], r_next, wave, k);   // batch 0 of page p_lo + 1
         });
         convert_q();
-        if constexpr (kSparse) {
-            mask_cur = join_mask(mkv0);
-            mask_next = join_mask(mkv1);
-        }
         __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
         wg_barrier();
 
         for (int p = p_lo; p < p_hi; ++p) {
             const LDS_AS uint8_t* tile = tiles[(p - p_lo) & 1];
             LDS_AS uint8_t* tnext = tiles[(p - p_lo + 1) & 1];
-            const int phys_next = load_phys(p + 3);
-            u32x2 mkv_after;
-            if constexpr (kSparse) mkv_after = load_mask(p + 2);
+            const int phys_next = kSparse ? 0 : load_phys(p + 3);
             Src r2;
             // hook h, slot k: store piece k of batch h (page p + 1) and load
             // piece k of the next batch into the freed slot; the last batch
@@ -609,7 +638,18 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
                     if constexpr (!Pieces::kHookPv[h] && ks >= at && (ks - at) % sd == 0 && (ks - at) / sd < kS)
                         move_piece(h_c, std::integral_constant<int, (ks - at) / sd>{});
                 });
-                if constexpr (ks == kKSteps - 1) r2 = page_rsrc(p + 2, phys2);
+                if constexpr (ks == kKSteps - 1) {
+                    if constexpr (kSparse) {
+                        // tile p + 2's rows have landed; tile p + 3's entries
+                        // (loaded a tile ago) go out for theirs; tile p + 4's
+                        // entries are loaded
+                        r2 = page_rsrc(p + 2, row_of(pend));
+                        pend = expand(p + 3, iv_next, mask3);
+                        iv_next = load_idx(p + 4);
+                    } else {
+                        r2 = page_rsrc(p + 2, phys2);
+                    }
+                }
             };
             auto pv_hook = [&](auto step_c) {
                 constexpr int step = decltype(step_c)::value;
@@ -625,8 +665,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
             r_next = r2;
             phys2 = phys_next;
             if constexpr (kSparse) {
-                mask_cur = mask_next;
-                mask_next = join_mask(mkv_after);
+                mask_cur = mask1;
+                mask1 = mask2;
+                mask2 = mask3;
             }
             __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);       // tile stores and reads retired
             wg_barrier();

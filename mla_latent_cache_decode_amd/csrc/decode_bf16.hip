@@ -722,7 +722,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t s
 
 hipError_t launch_decode_bf16_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                                      hipEvent_t ev_stop) {
-    // the gather goes through the row table: the page-block size is the pre-pass's business
+    // rows are gathered one by one: the page-block size enters only as a shift
     return launch_with_events(mla_decode_bf16_kernel<64, true>, dim3(a.num_workers * row_groups), stream, ev_start, ev_stop, a);
 }
 

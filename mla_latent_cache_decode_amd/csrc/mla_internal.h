@@ -61,39 +61,20 @@ struct DecodeArgs {
     int32_t min_quota;          // lower bound on cost units per worker
     float scale_log2;           // softmax_scale * log2(e)
     // sparse (top-k) decode: batch counts (sequence, query position) units of
-    // n_h rows each (s_q = 1 here), every unit topk tokens long; the tokens
-    // of tile p of unit u are gathered through the row table built by the
-    // sparse_rows pre-pass.  sparse_topk = 0: the dense decode.
+    // n_h rows each (s_q = 1 here), every unit topk entries long; the
+    // kernels read each unit's index list and turn its valid entries into
+    // cache rows through the block table of its sequence.  sparse_topk = 0:
+    // the dense decode.
     int32_t sparse_topk;
-    const uint32_t* sparse_rows;   // [units][tiles][32 pairs]: see SparseRowsArgs
-    const uint64_t* sparse_masks;  // [units][tiles]: bit t = token t of the tile takes part
-    const uint8_t* sparse_zero_row; // kSparseZeroRowBytes of zeros: what entries that do not take part fetch
-    // the bf16 sparse decode reads the index lists itself (no pre-pass):
     const int32_t* sparse_indices;  // [units][topk] token positions
     int32_t sparse_sq;              // query positions per sequence (unit u = b * sparse_sq + j)
 };
 
-// Pre-pass of the sparse decode: turns each unit's index list into physical
-// row ids (page * page_size + slot; kNoRow when the entry does not take
-// part) and per-tile masks.  Within a tile, the ids of tokens x and x + 8 of
-// each 16-token quarter w sit side by side, at pair w * 8 + x, so that a
-// lane of the decode fetches both of its tokens' ids with one 8-byte load.
+// A sparse entry that does not take part has no row (row ids are
+// page * page_size + slot); it is gathered from a row of zeros of
+// kSparseZeroRowBytes that each kernel keeps in device memory.
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;
 constexpr int kSparseZeroRowBytes = 2048;      // >= one bf16 row (1152 B)
-struct SparseRowsArgs {
-    const int32_t* indices;     // [units][topk] token positions
-    const int32_t* block_table; // [B][max_blocks]
-    const int32_t* seq_lens;    // [B]
-    uint32_t* rows;             // [units][tiles][64]
-    uint64_t* masks;            // [units][tiles]
-    uint8_t* zero_row;          // kSparseZeroRowBytes, zeroed by the pre-pass
-    int32_t units;              // B * s_q
-    int32_t s_q;
-    int32_t topk;
-    int32_t tiles;              // ceil(topk / 64)
-    int32_t max_blocks;
-    int32_t page_size;
-};
 
 struct CombineArgs {
     PlanView plan;
@@ -116,7 +97,6 @@ hipError_t launch_decode_bf16_sparse(const DecodeArgs& a, int row_groups, hipStr
                                      hipEvent_t ev_stop);
 hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                                     hipEvent_t ev_stop, bool fp4 = false);
-hipError_t launch_sparse_rows(const SparseRowsArgs& a, hipStream_t stream);
 // max_splits: an upper bound on the splits of one sequence (the worker
 // count); it sizes the combine's LDS and picks its shape.
 hipError_t launch_combine(const CombineArgs& a, int max_splits, hipStream_t stream);

@@ -160,7 +160,7 @@ def test_sparse_error_paths():
     assert lib.mla_decode_sparse_run(*args(k, ws.numel(), None)) == m.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_decode_sparse_run(*args(k, ws.numel(), idx + 2)) == m.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_decode_sparse_run(*args(k, 64, idx)) == m.MLA_ERR_WORKSPACE_TOO_SMALL
-    # the bf16 decode keeps no per-entry table: topk does not change the size
+    # the decode keeps no per-entry table: topk does not change the size
     assert dec.sparse_workspace_size(B, 4 * k) == dec.sparse_workspace_size(B, k)
     assert lib.mla_decode_sparse_run(*args((1 << 20) + 1, ws.numel(), idx)) == m.MLA_ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
