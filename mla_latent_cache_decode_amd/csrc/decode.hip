@@ -72,6 +72,9 @@ constexpr int kLdsBytes = kLdsTiles + kQLdsBytes;  // 163840 = all of a CU's LDS
 // tokens 16w .. 16w + 15 in pieces k < 9: lane i carries token 16w + (i & 15),
 // codes 16j .. 16j + 15 with j = 4k + (i >> 4), and their scale byte j / 2.
 // The 16 dequantised halves are tile chunks 2j and 2j + 1 of that token.
+// The scale bytes come once per page: each lane loads its token's 18 bytes
+// (one 16-byte and one 4-byte load) before the page's first store, in place
+// of one byte load per piece.
 struct Fp8Pieces {
     static constexpr int kPieces = 9;
     // three batches of three pieces
@@ -83,7 +86,11 @@ struct Fp8Pieces {
     static constexpr int kHookStride[3] = {5, 5, 10};
     struct Stage {
         u32x4 codes;
-        uint32_t scale;
+    };
+    // the e8m0 scales of the lane's token: bytes 0..15 and 16..17 (+ 2 pad)
+    struct PageScales {
+        u32x4 lo;
+        uint32_t hi;
     };
 
     int src_lane;       // (token - tok0) * 608 + 16 * (i >> 4), inside the wave's page
@@ -97,25 +104,34 @@ struct Fp8Pieces {
     }
     __device__ __forceinline__ void issue(Stage& s, __amdgpu_buffer_rsrc_t r, int, int k) const {
         s.codes = __builtin_amdgcn_raw_buffer_load_b128(r, pinned(src_lane) + k * 64, 0, 0);
-        // the scale byte of codes 16j.. sits at token * 608 + 576 + j / 2;
-        // derived here rather than held, to spare a register
-        const int l = opaque_lane();
-        const int scl = pinned(src_lane) - ((l >> 4) << 4) + kD + (l >> 5);
-        s.scale = __builtin_amdgcn_raw_buffer_load_b8(r, scl + k * 2, 0, 0);
     }
     // sparse gather: the lane's token row starts at `row` (anywhere in the
-    // cache, or the workspace's zero row for an entry that does not take part)
+    // cache, or a row of zeros for an entry that does not take part)
     __device__ __forceinline__ void issue(Stage& s, const uint8_t* row, int, int k) const {
         const int l = opaque_lane();
         s.codes = *(const u32x4*)(row + ((l >> 4) << 4) + k * 64);
-        s.scale = row[kD + (l >> 5) + k * 2];
     }
-    __device__ __forceinline__ void store(const Stage& s, LDS_AS uint8_t* tile, int, int k) const {
+    // the scales of the lane's token sit at token * 608 + 576 (16-byte aligned)
+    __device__ __forceinline__ void load_scales(PageScales& sc, __amdgpu_buffer_rsrc_t r) const {
+        const int l = opaque_lane();
+        const int off = pinned(src_lane) - ((l >> 4) << 4) + kD;
+        sc.lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        sc.hi = __builtin_amdgcn_raw_buffer_load_b32(r, off + 16, 0, 0);
+    }
+    __device__ __forceinline__ void load_scales(PageScales& sc, const uint8_t* row) const {
+        sc.lo = *(const u32x4*)(row + kD);
+        sc.hi = *(const uint32_t*)(row + kD + 16);
+    }
+    __device__ __forceinline__ void store(const Stage& s, const PageScales& sc, LDS_AS uint8_t* tile, int,
+                                          int k) const {
+        // the scale of codes 16j.. is byte j / 2 = 2k + (i >> 5) of the token's scales
+        const int h8 = (opaque_lane() >> 5) << 3;
+        const uint32_t word = k < 8 ? sc.lo[k >> 1] : sc.hi;
         // 2^(e-127) as fp32 bits e << 23.  e = 255 (NaN) also sets the top
         // mantissa bit, making a quiet NaN instead of infinity.  e = 0 gives
         // 0 rather than 2^-127: every e4m3 value times 2^-127 rounds to a
         // signed zero in fp16 anyway, so the dequantised halves are the same.
-        const uint32_t e = s.scale & 0xFF;
+        const uint32_t e = __builtin_amdgcn_ubfe(word, (uint32_t)((k & 1) * 16 + h8), 8);
         const uint32_t bits = (((e + 1) >> 8) << 22) | (e << 23);
         const float scale = __builtin_bit_cast(float, bits);
         // chunks 2j and 2j + 1 sit in adjacent 16-byte slots (the swizzle
@@ -154,6 +170,8 @@ struct Fp4Pieces {
         u32x2 codes;
         uint32_t scale;
     };
+    // the fp4 scales travel with each piece
+    struct PageScales {};
 
     int src_lane;       // (token - tok0) * 336 + 8 * (i >> 4), inside the wave's page
     int dst_lane;       // tile_off(token, 2 * (i >> 4)) without the column block
@@ -175,7 +193,9 @@ struct Fp4Pieces {
         s.codes = *(const u32x2*)(row + ((l >> 4) << 3) + k * 32);
         s.scale = row[kD / 2 + (l >> 4) + k * 4];
     }
-    __device__ __forceinline__ void store(const Stage& s, LDS_AS uint8_t* tile, int, int k) const {
+    __device__ __forceinline__ void load_scales(PageScales&, __amdgpu_buffer_rsrc_t) const {}
+    __device__ __forceinline__ void load_scales(PageScales&, const uint8_t*) const {}
+    __device__ __forceinline__ void store(const Stage& s, const PageScales&, LDS_AS uint8_t* tile, int, int k) const {
         // the e8m0 scale as fp32 bits, as for the fp8 rows
         const uint32_t e = s.scale & 0xFF;
         const float scale = __builtin_bit_cast(float, (((e + 1) >> 8) << 22) | (e << 23));
@@ -589,6 +609,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
 
         const Src r0 = page_rsrc(p_lo, phys0);
         Stage stg[kS], s0p[kPieces];
+        // the scales of the page whose pieces are stored next
+        typename Pieces::PageScales sc;
+        pc.load_scales(sc, r0);
         static_for<0, kPieces>([&](auto k) { pc.issue(s0p[k], r0, wave, k); });
         {
             const int row = active ? row0 + (lane0 & 31) : 0;
@@ -604,9 +627,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
 #pragma unroll
         for (int md = 0; md < kMdBlocks; ++md) st.o[md] = f32x16{};
         static_for<0, kPieces>([&](auto k) {
-            pc.store(s0p[k], tiles[0], wave, k);
+            pc.store(s0p[k], sc, tiles[0], wave, k);
             if constexpr (k < Pieces::first(1)) pc.issue(stg[k], r_next, wave, k);   // batch 0 of page p_lo + 1
         });
+        pc.load_scales(sc, r_next);
         convert_q();
         __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
         wg_barrier();
@@ -622,7 +646,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
             auto move_piece = [&](auto h_c, auto k_c) {
                 constexpr int h = decltype(h_c)::value, k = decltype(k_c)::value;
                 constexpr int n = Pieces::first(h) + k;
-                if constexpr (n < Pieces::first(h + 1)) pc.store(stg[k], tnext, wave, n);
+                if constexpr (n < Pieces::first(h + 1)) pc.store(stg[k], sc, tnext, wave, n);
+                // page p + 1 is stored: the scales of page p + 2 follow
+                if constexpr (n == kPieces - 1) pc.load_scales(sc, r2);
                 if constexpr (h + 1 < kNB) {
                     constexpr int n2 = Pieces::first(h + 1) + k;
                     if constexpr (n2 < Pieces::first(h + 2)) pc.issue(stg[k], r_next, wave, n2);

@@ -75,3 +75,28 @@ def test_one_million_token_context():
     ro, rl = mla_decode_ref(w.q_bits, w.pool, w.block_table, w.seq_lens, kv_dtype="bf16", d_c=512, d_r=64,
                             page=64, softmax_scale=spec.softmax_scale, heads=heads)
     assert_parity(w, out, lse, ro, rl, heads=heads)
+
+
+@pytest.mark.parametrize("kv_dtype,page", [("bf16", 64), ("fp8", 256)])
+def test_sparse_one_million_token_context(kv_dtype, page):
+    # index lists spread over a 1M-token context: page ids up to 16K (4K at
+    # block 256) pass through the kernels' own list-to-row translation
+    spec = WorkloadSpec(f"sparse_ctx1m_{kv_dtype}", 1, ("fixed", (1 << 20,)), s_q=2, topk=2048, page=page,
+                        kv_dtype=kv_dtype, spare_pages=2, seed=69, q_scale=0.5,
+                        outlier_p=0.01 if kv_dtype == "fp8" else 0.0, outlier_mult=20.0)
+    w = make_workload(spec)
+    assert int(w.indices.max()) > (1 << 20) - 4096
+    dev = torch.device("cuda:0")
+    t = to_torch(w, dev)
+    dec = make_decoder(w)
+    say(f"sparse {spec.name} page={page}")
+    out = torch.full((1, 2, 128, 512), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((1, 2, 128), float("nan"), dtype=torch.float32, device=dev)
+    dec.run_sparse(t["q"], t["kv"], t["block_table"], t["seq_lens"], t["indices"], out, lse)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    heads = [0, 77, 127]
+    ro, rl = mla_sparse_decode_ref(w.q_bits, w.pool, w.block_table, w.seq_lens, w.indices, kv_dtype=kv_dtype,
+                                   d_c=512, d_r=64, page=page, softmax_scale=spec.softmax_scale, heads=heads)
+    assert_parity(w, out, lse, ro, rl, heads=heads)
