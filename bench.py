@@ -135,9 +135,12 @@ def main():
     s = w.spec
     dev = torch.device("cuda:0")
     t = to_torch(w, dev)
+    # the cache tensor is the whole page pool: declare when it fits the
+    # 32-bit gather window (used by the bf16 sparse decode only)
+    flags = mla.MLA_FLAG_KV_WITHIN_4GIB if t["kv"].numel() <= mla.KV_WINDOW_BYTES else 0
     dec = mla.MlaDecode(max_batch=s.batch, s_q=s.s_q, n_h=s.n_h, d_c=s.d_c, d_r=s.d_r, block_size=s.page,
                         max_blocks_per_seq=w.block_table.shape[1], kv_dtype=s.kv_dtype,
-                        softmax_scale=s.softmax_scale, num_workers=args.num_workers)
+                        softmax_scale=s.softmax_scale, num_workers=args.num_workers, flags=flags)
     sparse = w.indices is not None
     ws = dec.alloc_sparse_workspace(s.batch, s.topk, device=dev) if sparse else dec.alloc_workspace(s.batch, device=dev)
     out = torch.empty((s.batch, s.s_q, s.n_h, s.d_c), dtype=torch.float32, device=dev)

@@ -21,4 +21,6 @@ from ._lib import (  # noqa: F401
     MLA_ERR_WORKSPACE_TOO_SMALL,
     MLA_ERR_HIP,
     MLA_ERR_OUT_OF_MEMORY,
+    MLA_FLAG_KV_WITHIN_4GIB,
+    KV_WINDOW_BYTES,
 )

@@ -23,6 +23,11 @@ MLA_ERR_WORKSPACE_TOO_SMALL = 3
 MLA_ERR_HIP = 4
 MLA_ERR_OUT_OF_MEMORY = 5
 
+# the caller guarantees the whole cache lies within 0xFFFFF000 bytes of its
+# base (include/mla_decode.h): the bf16 sparse gather then uses 32-bit offsets
+MLA_FLAG_KV_WITHIN_4GIB = 1
+KV_WINDOW_BYTES = 0xFFFFF000
+
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3_E8M0 = 1
 MLA_KV_FP4_E2M1_E8M0 = 2

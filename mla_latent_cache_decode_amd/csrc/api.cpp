@@ -135,7 +135,7 @@ mla_status_t validate_params(const mla_decode_params_t* p) {
         return MLA_ERR_INVALID_ARGUMENT;
     if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
     if (p->num_workers < 0 || p->num_workers > mla::kMaxWorkers) return MLA_ERR_INVALID_ARGUMENT;
-    if (p->flags != MLA_FLAG_NONE) return MLA_ERR_INVALID_ARGUMENT;
+    if ((p->flags & ~MLA_FLAG_KV_WITHIN_4GIB) != 0) return MLA_ERR_INVALID_ARGUMENT;
     if ((p->d_c + p->d_r) % 32 != 0 && p->kv_dtype != MLA_KV_BF16) return MLA_ERR_INVALID_ARGUMENT;
     // valid requests outside what this build instantiates
     if (p->d_c != mla::kDc || p->d_r != mla::kDr) return MLA_ERR_UNSUPPORTED;
@@ -330,7 +330,8 @@ mla_status_t mla_decode_sparse_run(mla_decode_handle_t h, const void* q, const v
     const hipEvent_t e0 = h->ev_start && h->ev_stop ? h->ev_start : nullptr;
     const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
     const hipError_t e = h->p.kv_dtype == MLA_KV_BF16
-                             ? mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1)
+                             ? mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1,
+                                                              (h->p.flags & MLA_FLAG_KV_WITHIN_4GIB) != 0)
                              : mla::launch_decode_fp8_sparse(da, l.row_groups, stream, e0, e1,
                                                              h->p.kv_dtype == MLA_KV_FP4_E2M1_E8M0);
     if (e != hipSuccess) return MLA_ERR_HIP;

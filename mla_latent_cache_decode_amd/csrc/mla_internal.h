@@ -74,6 +74,15 @@ struct DecodeArgs {
 // page * page_size + slot); it is gathered from a row of zeros of
 // kSparseZeroRowBytes that each kernel keeps in device memory.
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;
+// With MLA_FLAG_KV_WITHIN_4GIB the bf16 sparse gather addresses rows inside
+// the first kGatherWindow bytes of the cache with 32-bit buffer offsets (rows
+// up to kGatherRowMax); kGatherNone lies past the window, so a load there
+// returns zeros.
+constexpr uint32_t kGatherWindow = 0xFFFFF000u;
+constexpr uint32_t kGatherRowMax = (kGatherWindow - 2 * 576) / (2 * 576);
+constexpr uint32_t kGatherNone = 0xFFFFFFF0u;
+static_assert((uint64_t)kGatherRowMax * 1152 + 1152 <= kGatherWindow, "a window row ends inside the window");
+static_assert(kGatherNone >= kGatherWindow, "the no-row offset lies past the window");
 constexpr int kSparseZeroRowBytes = 2048;      // >= one bf16 row (1152 B)
 
 struct CombineArgs {
@@ -93,8 +102,9 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t s
 // the fp8-family kernel serves both quantised formats (fp4: the e2m1 row)
 hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                              hipEvent_t ev_stop, bool fp4 = false);
+// window: the cache lies in the first kGatherWindow bytes (MLA_FLAG_KV_WITHIN_4GIB)
 hipError_t launch_decode_bf16_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                                     hipEvent_t ev_stop);
+                                     hipEvent_t ev_stop, bool window);
 hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                                     hipEvent_t ev_stop, bool fp4 = false);
 // max_splits: an upper bound on the splits of one sequence (the worker

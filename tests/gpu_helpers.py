@@ -23,12 +23,12 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def make_decoder(w: Workload, num_workers: int = 0, max_batch=None):
+def make_decoder(w: Workload, num_workers: int = 0, max_batch=None, flags: int = 0):
     from mla_latent_cache_decode_amd import MlaDecode
     s = w.spec
     return MlaDecode(max_batch=max_batch or max(s.batch, 1), s_q=s.s_q, n_h=s.n_h, d_c=s.d_c, d_r=s.d_r,
                      block_size=s.page, max_blocks_per_seq=w.block_table.shape[1], kv_dtype=s.kv_dtype,
-                     softmax_scale=s.softmax_scale, num_workers=num_workers)
+                     softmax_scale=s.softmax_scale, num_workers=num_workers, flags=flags)
 
 
 def run_gpu(w: Workload, num_workers: int = 0, with_lse: bool = True, tensors=None, dec=None):

@@ -15,14 +15,14 @@ from gpu_helpers import assert_parity, make_decoder, run_gpu, say
 pytestmark = pytest.mark.gpu
 
 
-def run_sparse(w, num_workers=0, indices=None, with_lse=True, dec=None, tensors=None):
+def run_sparse(w, num_workers=0, indices=None, with_lse=True, dec=None, tensors=None, flags=0):
     s = w.spec
     dev = torch.device("cuda:0")
     t = tensors if tensors is not None else to_torch(w, dev)
     idx = t["indices"] if indices is None else torch.from_numpy(np.ascontiguousarray(indices)).to(dev)
-    dec = dec or make_decoder(w, num_workers)
+    dec = dec or make_decoder(w, num_workers, flags=flags)
     say(f"sparse decode {s.name} B={s.batch} s_q={s.s_q} n_h={s.n_h} topk={idx.shape[2]} page={s.page} "
-        f"workers={dec.info()['num_workers']} seed={s.seed}")
+        f"workers={dec.info()['num_workers']} flags={flags} seed={s.seed}")
     out = torch.full((s.batch, s.s_q, s.n_h, s.d_c), float("nan"), dtype=torch.float32, device=dev)
     lse = torch.full((s.batch, s.s_q, s.n_h), float("nan"), dtype=torch.float32, device=dev) if with_lse else None
     dec.run_sparse(t["q"], t["kv"], t["block_table"], t["seq_lens"], idx, out, lse)
@@ -60,20 +60,25 @@ VARIANTS = [
 ]
 
 
+WINDOW = 1   # MLA_FLAG_KV_WITHIN_4GIB: these caches are far smaller
+
+
 @pytest.mark.parametrize("spec", VARIANTS, ids=[s.name for s in VARIANTS])
 @pytest.mark.parametrize("workers", [0, 1, 3, 300])
-def test_sparse_parity_small(spec, workers):
+@pytest.mark.parametrize("flags", [0, WINDOW], ids=["addr64", "window"])
+def test_sparse_parity_small(spec, workers, flags):
     w = make_workload(spec)
-    out, lse = run_sparse(w, num_workers=workers)
+    out, lse = run_sparse(w, num_workers=workers, flags=flags)
     ro, rl = sparse_oracle(w)
     assert_parity(w, out, lse, ro, rl)
 
 
 @pytest.mark.parametrize("name", ["sparse_topk2048_b64", "sparse_fp8_topk2048_b64"])
-def test_sparse_full_size_sampled(name):
+@pytest.mark.parametrize("flags", [0, WINDOW], ids=["addr64", "window"])
+def test_sparse_full_size_sampled(name, flags):
     w = make_workload(name)
     batches = sorted({0, 31, 63, int(np.argmax(w.seq_lens))})
-    out, lse = run_sparse(w)
+    out, lse = run_sparse(w, flags=flags)
     ro, rl = sparse_oracle(w, batches=batches)
     assert_parity(w, out, lse, ro, rl, batches=batches)
     assert np.isfinite(out).all() and np.isfinite(lse).all()
@@ -124,10 +129,11 @@ def test_sparse_over_whole_context_equals_dense_bitwise(kv_dtype):
     idx = np.full_like(w.indices, -1)
     for b in range(spec.batch):
         idx[b, 0, :w.seq_lens[b]] = np.arange(w.seq_lens[b])
-    o_s, l_s = run_sparse(w, indices=idx, num_workers=1)
     o_d, l_d = run_gpu(w, num_workers=1)
-    np.testing.assert_array_equal(o_s, o_d)
-    np.testing.assert_array_equal(l_s, l_d)
+    for flags in (0, WINDOW):
+        o_s, l_s = run_sparse(w, indices=idx, num_workers=1, flags=flags)
+        np.testing.assert_array_equal(o_s, o_d)
+        np.testing.assert_array_equal(l_s, l_d)
 
 
 def test_sparse_repeat_bitwise_and_without_lse():
@@ -165,3 +171,62 @@ def test_sparse_error_paths():
     assert lib.mla_decode_sparse_run(*args((1 << 20) + 1, ws.numel(), idx)) == m.MLA_ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
     assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_sparse_rows_beyond_4gib(kv_dtype):
+    # The bf16 gather addresses rows in the first 4 GiB of the cache through
+    # 32-bit offsets and falls back to 64-bit addresses for a tile that holds
+    # a row beyond.  Odd pages move past 5 GiB into a cache whose other bytes
+    # are NaN: tiles mix both kinds of rows, and the result must be bitwise
+    # the one from the compact cache.
+    base = SMALL if kv_dtype == "bf16" else SPECS["sparse_fp8_topk2048_b64_small"]
+    w = make_workload(dataclasses.replace(base, name=f"sparse_far_{kv_dtype}", s_q=2, seed=55))
+    dev = torch.device("cuda:0")
+    t = to_torch(w, dev)
+    o1, l1 = run_sparse(w, num_workers=7, tensors=t)
+    kv = t["kv"]
+    n_pages, page_bytes = kv.shape[0], kv.shape[1] * kv.shape[2]
+    high = (5 << 30) // page_bytes
+    say(f"sparse far rows: {n_pages} pages, odd ones from page {high} ({high * page_bytes / 2**30:.2f} GiB) on")
+    big = torch.full((high + n_pages,) + tuple(kv.shape[1:]), 0xFF, dtype=kv.dtype, device=dev)
+    pages = torch.arange(n_pages, device=dev)
+    new = torch.where(pages % 2 == 0, pages, pages + high)
+    big[new] = kv
+    bt = t["block_table"].clone()
+    valid = bt >= 0
+    bt[valid] = new[bt[valid].long()].to(bt.dtype)
+    o2, l2 = run_sparse(w, num_workers=7, tensors=dict(t, kv=big, block_table=bt))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    del big
+    torch.cuda.empty_cache()
+
+
+def test_sparse_window_flag_never_reads_past_the_window():
+    # a caller that sets the 32-bit window flag for a cache larger than the
+    # window gets zeros for the rows past it (odd pages here), not an access
+    # outside it; rows inside keep their values
+    w = make_workload(dataclasses.replace(SMALL, name="sparse_window_broken", seed=56))
+    dev = torch.device("cuda:0")
+    t = to_torch(w, dev)
+    kv = t["kv"]
+    n_pages, page_bytes = kv.shape[0], kv.shape[1] * kv.shape[2]
+    high = (5 << 30) // page_bytes
+    big = torch.zeros((high + n_pages,) + tuple(kv.shape[1:]), dtype=kv.dtype, device=dev)
+    pages = torch.arange(n_pages, device=dev)
+    new = torch.where(pages % 2 == 0, pages, pages + high)
+    big[new] = kv
+    bt = t["block_table"].clone()
+    valid = bt >= 0
+    bt[valid] = new[bt[valid].long()].to(bt.dtype)
+    say("sparse window flag with rows past the window")
+    o, l_ = run_sparse(w, num_workers=7, tensors=dict(t, kv=big, block_table=bt), flags=WINDOW)
+    assert np.isfinite(o).all() and np.isfinite(l_).all()
+    # the oracle on a cache whose odd pages are zero
+    pool = w.pool.copy()
+    pool[1::2] = 0
+    ro, rl = sparse_oracle(dataclasses.replace(w, pool=pool))
+    assert_parity(w, o, l_, ro, rl)
+    del big
+    torch.cuda.empty_cache()
