@@ -136,7 +136,7 @@ def main():
     dev = torch.device("cuda:0")
     t = to_torch(w, dev)
     # the cache tensor is the whole page pool: declare when it fits the
-    # 32-bit gather window (used by the bf16 sparse decode only)
+    # 32-bit gather window (used by the sparse decode only)
     flags = mla.MLA_FLAG_KV_WITHIN_4GIB if t["kv"].numel() <= mla.KV_WINDOW_BYTES else 0
     dec = mla.MlaDecode(max_batch=s.batch, s_q=s.s_q, n_h=s.n_h, d_c=s.d_c, d_r=s.d_r, block_size=s.page,
                         max_blocks_per_seq=w.block_table.shape[1], kv_dtype=s.kv_dtype,

@@ -70,10 +70,10 @@ typedef enum mla_kv_dtype {
 #define MLA_FLAG_NONE 0
 /* The caller guarantees that every page it will pass lies within the first
  * 0xFFFFF000 bytes (4 GiB - 4 KiB) from the kv_pages pointer of each run
- * call.  The bf16 sparse decode then gathers rows with 32-bit offsets, which
+ * call.  The sparse decode then gathers rows with 32-bit offsets, which
  * issue faster; without the flag it uses 64-bit addresses.  A row past that
  * window under the flag reads as zeros (a wrong result, never an access
- * outside the window).  No other path is affected. */
+ * outside the window).  The dense decode is not affected. */
 #define MLA_FLAG_KV_WITHIN_4GIB 1
 
 typedef struct mla_decode_params {

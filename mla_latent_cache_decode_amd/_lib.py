@@ -24,7 +24,7 @@ MLA_ERR_HIP = 4
 MLA_ERR_OUT_OF_MEMORY = 5
 
 # the caller guarantees the whole cache lies within 0xFFFFF000 bytes of its
-# base (include/mla_decode.h): the bf16 sparse gather then uses 32-bit offsets
+# base (include/mla_decode.h): the sparse gathers then use 32-bit offsets
 MLA_FLAG_KV_WITHIN_4GIB = 1
 KV_WINDOW_BYTES = 0xFFFFF000
 

@@ -329,11 +329,11 @@ mla_status_t mla_decode_sparse_run(mla_decode_handle_t h, const void* q, const v
     da.sparse_sq = h->p.s_q;
     const hipEvent_t e0 = h->ev_start && h->ev_stop ? h->ev_start : nullptr;
     const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
+    const bool window = (h->p.flags & MLA_FLAG_KV_WITHIN_4GIB) != 0;
     const hipError_t e = h->p.kv_dtype == MLA_KV_BF16
-                             ? mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1,
-                                                              (h->p.flags & MLA_FLAG_KV_WITHIN_4GIB) != 0)
+                             ? mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1, window)
                              : mla::launch_decode_fp8_sparse(da, l.row_groups, stream, e0, e1,
-                                                             h->p.kv_dtype == MLA_KV_FP4_E2M1_E8M0);
+                                                             h->p.kv_dtype == MLA_KV_FP4_E2M1_E8M0, window);
     if (e != hipSuccess) return MLA_ERR_HIP;
 
     mla::CombineArgs ca{};

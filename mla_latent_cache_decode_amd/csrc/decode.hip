@@ -95,9 +95,10 @@ struct Fp8Pieces {
 
     int src_lane;       // (token - tok0) * 608 + 16 * (i >> 4), inside the wave's page
     int dst_lane;       // tile_off(token, 2 * (i >> 4)) without the column block
+    __amdgpu_buffer_rsrc_t win;   // the declared cache window (sparse gather)
 
     // tok0: the tile token at which the wave's page descriptor starts
-    __device__ __forceinline__ Fp8Pieces(int lane, int wave, int tok0) {
+    __device__ __forceinline__ Fp8Pieces(int lane, int wave, int tok0, __amdgpu_buffer_rsrc_t w) : win(w) {
         const int t = wave * 16 + (lane & 15);
         src_lane = (t - tok0) * kFp8RowBytes + ((lane >> 4) << 4);
         dst_lane = tile_off(t, 2 * (lane >> 4));
@@ -111,6 +112,12 @@ struct Fp8Pieces {
         const int l = opaque_lane();
         s.codes = *(const u32x4*)(row + ((l >> 4) << 4) + k * 64);
     }
+    // sparse gather inside the declared window: the row at byte offset `row`
+    // of window descriptor `win` (an offset past the window reads zeros)
+    __device__ __forceinline__ void issue(Stage& s, uint32_t row, int, int k) const {
+        const int l = opaque_lane();
+        s.codes = __builtin_amdgcn_raw_buffer_load_b128(win, (int)(row + ((l >> 4) << 4) + k * 64), 0, 0);
+    }
     // the scales of the lane's token sit at token * 608 + 576 (16-byte aligned)
     __device__ __forceinline__ void load_scales(PageScales& sc, __amdgpu_buffer_rsrc_t r) const {
         const int l = opaque_lane();
@@ -121,6 +128,10 @@ struct Fp8Pieces {
     __device__ __forceinline__ void load_scales(PageScales& sc, const uint8_t* row) const {
         sc.lo = *(const u32x4*)(row + kD);
         sc.hi = *(const uint32_t*)(row + kD + 16);
+    }
+    __device__ __forceinline__ void load_scales(PageScales& sc, uint32_t row) const {
+        sc.lo = __builtin_amdgcn_raw_buffer_load_b128(win, (int)(row + kD), 0, 0);
+        sc.hi = __builtin_amdgcn_raw_buffer_load_b32(win, (int)(row + kD + 16), 0, 0);
     }
     __device__ __forceinline__ void store(const Stage& s, const PageScales& sc, LDS_AS uint8_t* tile, int,
                                           int k) const {
@@ -175,8 +186,9 @@ struct Fp4Pieces {
 
     int src_lane;       // (token - tok0) * 336 + 8 * (i >> 4), inside the wave's page
     int dst_lane;       // tile_off(token, 2 * (i >> 4)) without the column block
+    __amdgpu_buffer_rsrc_t win;   // the declared cache window (sparse gather)
 
-    __device__ __forceinline__ Fp4Pieces(int lane, int wave, int tok0) {
+    __device__ __forceinline__ Fp4Pieces(int lane, int wave, int tok0, __amdgpu_buffer_rsrc_t w) : win(w) {
         const int t = wave * 16 + (lane & 15);
         src_lane = (t - tok0) * kFp4RowBytes + ((lane >> 4) << 3);
         dst_lane = tile_off(t, 2 * (lane >> 4));
@@ -193,8 +205,15 @@ struct Fp4Pieces {
         s.codes = *(const u32x2*)(row + ((l >> 4) << 3) + k * 32);
         s.scale = row[kD / 2 + (l >> 4) + k * 4];
     }
+    __device__ __forceinline__ void issue(Stage& s, uint32_t row, int, int k) const {
+        const int l = opaque_lane();
+        s.codes = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(win, (int)(row + ((l >> 4) << 3) + k * 32), 0, 0));
+        s.scale = __builtin_amdgcn_raw_buffer_load_b8(win, (int)(row + kD / 2 + (l >> 4) + k * 4), 0, 0);
+    }
     __device__ __forceinline__ void load_scales(PageScales&, __amdgpu_buffer_rsrc_t) const {}
     __device__ __forceinline__ void load_scales(PageScales&, const uint8_t*) const {}
+    __device__ __forceinline__ void load_scales(PageScales&, uint32_t) const {}
     __device__ __forceinline__ void store(const Stage& s, const PageScales&, LDS_AS uint8_t* tile, int, int k) const {
         // the e8m0 scale as fp32 bits, as for the fp8 rows
         const uint32_t e = s.scale & 0xFF;
@@ -392,7 +411,10 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
 // loads, whose results give tile p + 3's rows one tile later.
 __device__ __attribute__((aligned(256))) uint8_t g_sparse_zero_row[kSparseZeroRowBytes] = {};
 
-template <int PS, bool kSparse, bool kFp4>
+// kWin (sparse only): the caller has declared that the whole cache lies in
+// the first kGatherWindow bytes from its base; rows are then gathered with
+// 32-bit buffer offsets.
+template <int PS, bool kSparse, bool kFp4, bool kWin = false>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArgs a) {
     typedef std::conditional_t<kFp4, Fp4Pieces, Fp8Pieces> Pieces;
     typedef PageGeom<PS> Geom;
@@ -510,7 +532,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         // (physical page phys) that the workgroup loads, size 0 past p_hi;
         // sparse: the lane's row (row id phys), or the zero row
         auto page_rsrc = [&](int p, int phys) {
-            if constexpr (kSparse) {
+            if constexpr (kSparse && kWin) {
+                // the row's byte offset in the window; kGatherWindow (past it,
+                // and past it still after a piece's offset is added) reads zeros
+                constexpr uint32_t kRowMax = (kGatherWindow - kRowBytes) / kRowBytes;
+                const bool live = p < p_hi && (uint32_t)phys != kNoRow && (uint32_t)phys <= kRowMax;
+                return live ? (uint32_t)phys * (uint32_t)kRowBytes : kGatherWindow;
+            } else if constexpr (kSparse) {
                 const bool live = p < p_hi && (uint32_t)phys != kNoRow;
                 return live ? a.kv + (uint64_t)(uint32_t)phys * kRowBytes : (const uint8_t*)g_sparse_zero_row;
             } else {
@@ -582,7 +610,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
                 *(LDS_AS f16x8*)(qr_lds + (ks - kQRegSteps) * 1024) = qf[ks];
         };
         const f16x8(&qreg)[kQRegSteps] = *reinterpret_cast<const f16x8(*)[kQRegSteps]>(&qf[0]);
-        const Pieces pc(opaque_lane(), wave, tok0);
+        const Pieces pc(opaque_lane(), wave, tok0, make_rsrc(a.kv, kWin ? (int)kGatherWindow : 0));
 
         // ---- Page pipeline, one barrier per tile.  Pieces stream through
         // VGPRs (converted or dequantised in registers) into the idle
@@ -756,8 +784,11 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t st
 }
 
 hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                                    hipEvent_t ev_stop, bool fp4) {
+                                    hipEvent_t ev_stop, bool fp4, bool window) {
     const dim3 grid(a.num_workers * row_groups);
+    if (window)
+        return fp4 ? launch_with_events(mla_decode_kernel<64, true, true, true>, grid, stream, ev_start, ev_stop, a)
+                   : launch_with_events(mla_decode_kernel<64, true, false, true>, grid, stream, ev_start, ev_stop, a);
     return fp4 ? launch_with_events(mla_decode_kernel<64, true, true>, grid, stream, ev_start, ev_stop, a)
                : launch_with_events(mla_decode_kernel<64, true, false>, grid, stream, ev_start, ev_stop, a);
 }

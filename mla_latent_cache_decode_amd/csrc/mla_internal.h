@@ -74,7 +74,7 @@ struct DecodeArgs {
 // page * page_size + slot); it is gathered from a row of zeros of
 // kSparseZeroRowBytes that each kernel keeps in device memory.
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;
-// With MLA_FLAG_KV_WITHIN_4GIB the bf16 sparse gather addresses rows inside
+// With MLA_FLAG_KV_WITHIN_4GIB the sparse gathers address rows inside
 // the first kGatherWindow bytes of the cache with 32-bit buffer offsets (rows
 // up to kGatherRowMax); kGatherNone lies past the window, so a load there
 // returns zeros.
@@ -106,7 +106,7 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t st
 hipError_t launch_decode_bf16_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                                      hipEvent_t ev_stop, bool window);
 hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                                    hipEvent_t ev_stop, bool fp4 = false);
+                                    hipEvent_t ev_stop, bool fp4, bool window);
 // max_splits: an upper bound on the splits of one sequence (the worker
 // count); it sizes the combine's LDS and picks its shape.
 hipError_t launch_combine(const CombineArgs& a, int max_splits, hipStream_t stream);

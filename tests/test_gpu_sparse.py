@@ -175,11 +175,10 @@ def test_sparse_error_paths():
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 def test_sparse_rows_beyond_4gib(kv_dtype):
-    # The bf16 gather addresses rows in the first 4 GiB of the cache through
-    # 32-bit offsets and falls back to 64-bit addresses for a tile that holds
-    # a row beyond.  Odd pages move past 5 GiB into a cache whose other bytes
-    # are NaN: tiles mix both kinds of rows, and the result must be bitwise
-    # the one from the compact cache.
+    # Without the window flag the gathers use 64-bit addresses: odd pages
+    # move past 5 GiB into a cache whose other bytes are NaN, tiles mix near
+    # and far rows, and the result must be bitwise the one from the compact
+    # cache.
     base = SMALL if kv_dtype == "bf16" else SPECS["sparse_fp8_topk2048_b64_small"]
     w = make_workload(dataclasses.replace(base, name=f"sparse_far_{kv_dtype}", s_q=2, seed=55))
     dev = torch.device("cuda:0")
@@ -203,11 +202,13 @@ def test_sparse_rows_beyond_4gib(kv_dtype):
     torch.cuda.empty_cache()
 
 
-def test_sparse_window_flag_never_reads_past_the_window():
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "fp4"])
+def test_sparse_window_flag_never_reads_past_the_window(kv_dtype):
     # a caller that sets the 32-bit window flag for a cache larger than the
     # window gets zeros for the rows past it (odd pages here), not an access
     # outside it; rows inside keep their values
-    w = make_workload(dataclasses.replace(SMALL, name="sparse_window_broken", seed=56))
+    base = SMALL if kv_dtype == "bf16" else SPECS["sparse_fp8_topk2048_b64_small"]
+    w = make_workload(dataclasses.replace(base, name=f"sparse_window_broken_{kv_dtype}", kv_dtype=kv_dtype, seed=56))
     dev = torch.device("cuda:0")
     t = to_torch(w, dev)
     kv = t["kv"]
