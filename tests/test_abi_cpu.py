@@ -94,6 +94,8 @@ def _init(**over):
     (dict(softmax_scale=-1.0), 1),
     (dict(num_workers=-1), 1),
     (dict(flags=4), 1),
+    (dict(flags=2), 1),          # only MLA_FLAG_KV_WITHIN_4GIB is defined
+    (dict(flags=-1), 1),
     (dict(d_c=448), 2),          # valid request, not instantiated in this build
     (dict(block_size=48), 2),    # page blocks: powers of two from 16 to 256
     (dict(block_size=8), 2),
@@ -121,11 +123,12 @@ def test_init_null_arguments():
 
 
 @pytest.mark.parametrize("block_size", [16, 32, 64, 128, 256])
-def test_valid_params_without_a_gpu_report_hip_error(block_size):
+@pytest.mark.parametrize("flags", [0, 1], ids=["no_flags", "kv_within_4gib"])
+def test_valid_params_without_a_gpu_report_hip_error(block_size, flags):
     import torch
     if torch.cuda.is_available():
         pytest.skip("this host has a GPU")
-    st, h = _init(block_size=block_size)
+    st, h = _init(block_size=block_size, flags=flags)
     assert st == 4 and h is None
 
 
