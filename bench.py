@@ -10,11 +10,25 @@ resident in HBM before the timed region.  ``--workload`` picks another
 recipe (a parity workload, or the sparse top-k one, whose step is the
 gathering decode, which reads the index lists itself, and the combine).
 
-Prints one JSON line: KV-read GB/s (whole job), TFLOP/s, the dominant
-kernel's roofline (decode kernel: algorithmic KV bytes per launch over its
-average duration, taken by HIP events recorded with the kernel's dispatch on
-every 8th step of the timed region; an evented step runs ~6 us longer, so
-the other steps run without them) and the float64 CPU oracle timed on a
+Order of the run, all on one stream:
+  1. W warm-up steps (--warmup), then a pre-roll of further untimed steps
+     until at least --preroll-ms of GPU time has passed: the GPU needs tens
+     of milliseconds of load to reach its steady clock (reported as
+     "preroll_steps").
+  2. Cold steps (--cold-steps): before each, a flush writes 1 GiB and then
+     reads another 1 GiB, so no byte of the step's inputs is left in the L2s
+     or the 256 MB last-level cache and no dirty line is left to write back;
+     each step is timed alone by events around it (the flush is outside).
+     Five untimed steps follow, back to the warm state.
+  3. The timed region: exactly K steps (--steps) back to back, warm cache,
+     bracketed by synchronisations: ``value`` and ``ms_per_step``.
+  4. A sampling pass of --kernel-samples more steps whose decode kernel is
+     timed by HIP events recorded with its own dispatch (these cost ~6 us a
+     step, so the timed region runs without them): the dominant kernel's
+     roofline.
+
+Prints one JSON line: KV-read GB/s (whole job), TFLOP/s, the cold-cache
+figures, the dominant kernel's roofline and the float64 CPU oracle timed on a
 bounded sample of the same workload.
 """
 
@@ -40,15 +54,17 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first: the GPU needs ~20 ms of load to reach its steady clock")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--preroll-ms", type=float, default=150.0,
+                    help="after the warm-up, untimed steps until this much GPU time has passed (steady clock)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps timed one by one after a cache flush (0: none)")
+    ap.add_argument("--kernel-samples", type=int, default=20,
+                    help="steps whose decode kernel is timed by dispatch events, after the timed region (>= 10)")
     ap.add_argument("--workload", default=None, help="workload name (default: the long-context one)")
     ap.add_argument("--num-workers", type=int, default=0)
     ap.add_argument("--cpu-budget-s", type=float, default=15.0, help="oracle sample budget (seconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="time the decode kernel with HIP events on every Nth step of the timed region "
-                         "(an evented step costs ~6 us more; the others run bare)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -163,37 +179,85 @@ def main():
         if st != 0:
             raise mla.MlaError(st, entry.__name__)
 
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # events that take the decode kernel's own start/end timestamps (recorded
-    # by the library with the kernel's dispatch, on this stream) on every
-    # event_every-th step of the timed region
-    every = max(args.event_every, 1)
-    sampled = [k for k in range(args.steps) if k % every == 0]
-    ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in sampled}
-    for a, b in ev.values():   # torch only reads events it has seen recorded
+    # pre-roll: untimed steps until --preroll-ms of GPU time has passed; the
+    # count comes from a first batch of 10, the rest is enqueued in one go
+    pre_steps, pre_ms = 0, 0.0
+    if args.preroll_ms > 0:
+        a, b = ev(), ev()
         a.record(stream)
+        for _ in range(10):
+            step()
         b.record(stream)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
+        b.synchronize()
+        per = max(a.elapsed_time(b) / 10, 1e-3)
+        more = int(math.ceil(max(args.preroll_ms - a.elapsed_time(b), 0.0) / per))
+        c = ev()
+        for _ in range(more):
+            step()
+        c.record(stream)
+        c.synchronize()
+        pre_steps, pre_ms = 10 + more, a.elapsed_time(c)
+    print(f"[bench] pre-roll {pre_steps} steps, {pre_ms:.1f} ms", file=sys.stderr, flush=True)
+
+    # cold steps: flush (write 1 GiB, then read another 1 GiB), then one step
+    # timed alone; its decode kernel by dispatch events
+    cold = None
+    if args.cold_steps > 0:
+        print(f"[bench] cold {args.cold_steps}", file=sys.stderr, flush=True)
+        flush_w = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush_r = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
+        c_step, c_kern = [], []
+        for k in range(args.cold_steps):
+            flush_w.fill_(k & 0xFF)
+            torch.sum(flush_r, dim=0, out=sink)
+            s0, s1, k0, k1 = ev(), ev(), ev(), ev()
+            lib.mla_decode_set_profile_events(dec._h, k0.cuda_event, k1.cuda_event)
+            s0.record(stream)
+            step()
+            s1.record(stream)
+            lib.mla_decode_set_profile_events(dec._h, None, None)
+            torch.cuda.synchronize()
+            c_step.append(s0.elapsed_time(s1))
+            c_kern.append(k0.elapsed_time(k1))
+        del flush_w, flush_r
+        cold = (float(np.median(c_step)), float(np.median(c_kern)), len(c_step))
+        for _ in range(5):      # back to the warm state before the timed region
+            step()
+
+    # the timed region: K bare steps back to back
+    t_start, t_stop = ev(), ev()
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t_start.record(stream)
-    for k in range(args.steps):
-        if k in ev:
-            lib.mla_decode_set_profile_events(dec._h, ev[k][0].cuda_event, ev[k][1].cuda_event)
-        elif k - 1 in ev:
-            lib.mla_decode_set_profile_events(dec._h, None, None)
+    for _ in range(args.steps):
         step()
     t_stop.record(stream)
     torch.cuda.synchronize()
-    lib.mla_decode_set_profile_events(dec._h, None, None)
     ms_total = t_start.elapsed_time(t_stop)
     ms_step = ms_total / args.steps
-    kernel_ms = [a.elapsed_time(b) for a, b in ev.values()]
+
+    # sampling pass: the decode kernel's own dispatch timestamps, every step
+    n_samp = max(args.kernel_samples, 10)
+    samp = [(ev(), ev()) for _ in range(n_samp)]
+    for a, b in samp:           # torch only reads events it has seen recorded
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for a, b in samp:
+        lib.mla_decode_set_profile_events(dec._h, a.cuda_event, b.cuda_event)
+        step()
+    lib.mla_decode_set_profile_events(dec._h, None, None)
+    torch.cuda.synchronize()
+    kernel_ms = [a.elapsed_time(b) for a, b in samp]
     kms = float(np.mean(kernel_ms))
 
     if args.copy_mb:
@@ -245,6 +309,7 @@ def main():
                    **({"topk": s.topk, "selected_tokens": w.selected_tokens} if sparse else {}),
                    "workers": info["num_workers"], "row_groups": info["row_groups"],
                    "compute_units": info["compute_units"]},
+        "preroll_steps": pre_steps,
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tflop_s": round(tflops, 2),
         "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -254,6 +319,15 @@ def main():
                      "bytes_per_launch": kv_bytes, "flop_per_launch": fl,
                      "intensity_flop_per_byte": round(intensity, 1), "kernel_gbs": round(k_gbs, 2)},
     }
+    if cold is not None:
+        c_step, c_kern, n_cold = cold
+        res["cold"] = {"what": "each step timed alone after a 1 GiB write + 1 GiB read flush (median)",
+                       "steps": n_cold, "ms_per_step": round(c_step, 5),
+                       "value": round(kv_bytes / (c_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+                       "kernel_ms": round(c_kern, 5),
+                       "kernel_gbs": round(kv_bytes / (c_kern * 1e-3) / 1e9, 2),
+                       "kernel_hbm_frac": round(kv_bytes / (c_kern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "kernel_tflop_s": round(fl / (c_kern * 1e-3) / 1e12, 2)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)

@@ -121,9 +121,12 @@ mla_status_t mla_decode_workspace_size(mla_decode_handle_t h, int32_t batch, siz
  *   kv_pages    : device, [num_pages][block_size][row_stride] in kv_dtype's row
  *                 format (see mla_kv_row_stride), 16-byte aligned.
  *   block_table : device, int32 [batch][max_blocks_per_seq]; entry [b][p] is the
- *                 physical page of logical page p of sequence b.  Only entries
- *                 p < ceil(seq_lens[b] / block_size) are read; they must be valid
- *                 page indices (precondition, not checked on the device).
+ *                 physical page of logical page p of sequence b.  Entries
+ *                 p < ceil(seq_lens[b] / block_size) must be valid page indices
+ *                 (precondition, not checked on the device).  The decode works
+ *                 on 64-token tiles: with block_size < 64 it may also read the
+ *                 entries up to the end of the sequence's last tile (within
+ *                 max_blocks_per_seq), but never dereferences them.
  *   seq_lens    : device, int32 [batch]; L_b counts every cached token including
  *                 the s_q new ones.  Query j of sequence b sees tokens
  *                 0 .. L_b - s_q + j (causal over the last s_q positions).
@@ -137,9 +140,24 @@ mla_status_t mla_decode_workspace_size(mla_decode_handle_t h, int32_t batch, siz
  *                 after the call.  Concurrent runs need distinct workspaces.
  *   hip_stream  : hipStream_t as void*, NULL = default stream.
  * Tail slots after a sequence's last token, unused pages and row padding are
- * never read, whatever they hold.  Results do not depend on how the context
- * is split across workers beyond fp32 rounding, and repeated calls with the
- * same inputs and handle are bitwise identical. */
+ * never read, whatever they hold.
+ *
+ * Value range (precondition).  The products run on 16-bit matrix cores with
+ * fp32 accumulation: bf16 cache values enter Q.K^T as they are, but P.V (and,
+ * for the quantised formats, both products) takes them converted to fp16.
+ * Every decoded cache element x of a visible token must therefore satisfy
+ * |x| < 65520 (every finite bf16 value up to 65280 in magnitude; an fp8 code
+ * times its scale up to 61440); a larger one becomes infinite and the output
+ * of its rows NaN.  Magnitudes below 2^-14 keep fewer significant bits, and
+ * those below 2^-25 become zero; both are far below the output tolerance
+ * whenever the values that dominate a row are of ordinary size.
+ *
+ * Split-KV: the context of a sequence is split across workers, and each
+ * split's normalised partial output is stored as fp16 (relative rounding
+ * 2^-11) before the fp32 log-sum-exp merge, so results depend on the split
+ * count (the handle's worker count) at that level, far inside the stated
+ * tolerance.  Repeated calls with the same inputs and handle are bitwise
+ * identical. */
 mla_status_t mla_decode_run(mla_decode_handle_t h,
                             const void* q,
                             const void* kv_pages,

@@ -12,8 +12,9 @@ Draw order (torch CPU generator, seeded per workload):
   1. seq_lens
   2. physical page permutation (unless the table is the identity)
   3. cache source values: float32 N(0,1), drawn in chunks of 256 pages
-     (for FP8 / FP4 first an outlier mask per chunk, then the values), then
-     rounded to bf16 (round-to-nearest-even) or quantised to FP8 / FP4
+     (for FP8 / FP4 first an outlier mask per chunk, then the values),
+     times the workload's kv scale, then rounded to bf16
+     (round-to-nearest-even) or quantised to FP8 / FP4
   4. queries: float32 N(0,1) times the workload's q scale, rounded to bf16
   5. sparse workloads only ("DeepSeek-V3.2" record: a top-k selector,
      index_topk = 2048, picks the tokens each query attends over): for every
@@ -56,6 +57,7 @@ class WorkloadSpec:
     page: int = 64
     table: str = "perm"             # "perm" | "identity"
     q_scale: float = 1.0
+    kv_scale: float = 1.0           # multiplies the cache source values before encoding
     outlier_p: float = 0.0
     outlier_mult: float = 1.0
     spare_pages: int = 64
@@ -288,6 +290,8 @@ def make_workload(spec: Union[str, WorkloadSpec], seed: Optional[int] = None) ->
             vals = torch.where(mask, vals * spec.outlier_mult, vals)
         else:
             vals = torch.randn((rows, d), generator=gen)
+        if spec.kv_scale != 1.0:
+            vals = vals * spec.kv_scale
         if spec.kv_dtype == "bf16":
             enc = vals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
             pool[phys[c0:c1]] = enc.reshape(c1 - c0, page, d)

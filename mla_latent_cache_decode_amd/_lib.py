@@ -14,7 +14,9 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmla_decode.so")
+# MLA_DECODE_LIB_PATH may name another build of the same sources (the host
+# AddressSanitizer build that the ABI test makes); by default the in-tree one
+LIB_PATH = os.environ.get("MLA_DECODE_LIB_PATH") or os.path.join(_PKG, "libmla_decode.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARGUMENT = 1

@@ -69,6 +69,32 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB_PATH
 
 
+def asan_runtime() -> str | None:
+    """The clang AddressSanitizer runtime that hipcc's host compiler links against."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_asan_host(verbose: bool = False) -> str:
+    """The same library with its host code (the C ABI in api.cpp) built under
+    AddressSanitizer; the kernel objects are the release ones.  Load it into a
+    process that preloads asan_runtime().  Returns its path."""
+    kernels = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s.endswith(".hip")]
+    if not all(os.path.exists(k) for k in kernels):
+        build(verbose)
+    out_dir = os.path.join(BUILD_DIR, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    obj = os.path.join(out_dir, "api.o")
+    # -Xarch_host before each sanitizer flag: host code only, never GPU code
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libasan"]
+    flags = [f for f in COMMON_FLAGS if f != "-O3"] + ["-O1", "-g"] + san
+    _run([HIPCC] + flags + ["-c", os.path.join(CSRC, "api.cpp"), "-o", obj], verbose)
+    lib = os.path.join(out_dir, "libmla_decode_asan.so")
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + san + ["-o", lib, obj] + kernels, verbose)
+    return lib
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)

@@ -592,9 +592,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
                 for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf((float)qb[e]));
             }
             qmax = pair_max(qmax);
-            // exponent of qmax (a normal or zero float after the bf16 widening)
+            // exponent of qmax (the bf16 widening keeps fp32's exponent range;
+            // a bf16 subnormal reads as exponent -127, zero is taken as 14).
+            // sh >= -100 keeps both factors normal floats: a head whose max
+            // |q| lies below 2^-86 is scaled by 2^100 only, and its scores,
+            // below 2^-60 in magnitude, give a flat softmax either way
             const int ex = qmax > 0.f ? (int)((__builtin_bit_cast(uint32_t, qmax) >> 23) & 0xFF) - 127 : 14;
-            const int sh = ex - 14;
+            const int sh = max(ex - 14, -100);
             const float down = __builtin_bit_cast(float, (uint32_t)(127 - sh) << 23);   // 2^-sh
             const float up = __builtin_bit_cast(float, (uint32_t)(127 + sh) << 23);     // 2^sh
 #pragma unroll

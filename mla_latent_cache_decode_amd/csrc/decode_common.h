@@ -294,8 +294,12 @@ __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_i
         }
         carry_cost += tc;
         carry_slot += ts;
-        // stop once past this worker's quota (sequences owned by it are then done too)
-        if (carry_cost >= w_hi) break;
+        // stop once past this worker's quota: the sequences it owns are then
+        // done too -- except for the last worker, which owns every empty
+        // sequence at the end of the cost axis (position total, which equals
+        // its w_hi when total is a multiple of the worker count) and so must
+        // scan every chunk
+        if (carry_cost >= w_hi && worker < G - 1) break;
     }
     __syncthreads();
     return ws;

@@ -39,7 +39,6 @@ and row padding are never touched) and then runs every step in float64.
 
 from __future__ import annotations
 
-import math
 from typing import Iterable, Optional
 
 import numpy as np
@@ -133,8 +132,3 @@ def mla_decode_ref(q_bits: np.ndarray, pool: np.ndarray, block_table: np.ndarray
             lse[b, j, head_idx] = l_
     return out, lse
 
-
-def default_softmax_scale(d_h: int = 128, d_r: int = 64) -> float:
-    """1/sqrt(d_h + d_R): the per-head query/key length before absorption
-    (d_h = 128 from section 1, d_R = 64 from section 1.1 of the guide)."""
-    return 1.0 / math.sqrt(d_h + d_r)

@@ -1,0 +1,150 @@
+"""The LDS tile layout of the decode kernels, checked exhaustively on the CPU.
+
+A 64-token tile of 16-bit elements is 9 column blocks of 64 dims; token t's
+16-byte chunk c sits at byte tile_off(t, c).  The two functions that define
+the layout, sw() and tile_off(), are read from the kernel header itself (their
+bodies are plain integer expressions, valid Python too), so an edit there is
+checked here.  The access patterns below restate, lane by lane, how the
+kernels address the tile:
+
+* the direct-to-LDS page loads of the bf16 kernel (each 1 KiB load writes
+  contiguous LDS, its lanes fetch the chunks the layout puts there),
+* the Q.K^T fragment reads (128-bit, both kernels),
+* the dequantised stores of the fp8 / fp4 pieces (128-bit),
+* the transposed V reads of P.V (ds_read_b64_tr_b16, both kernels).
+
+LDS bank model: 64 banks of 4 bytes.  A 128-bit access is served 16 lanes at
+a time (16 x 16 B = one pass over the 64 banks), a 64-bit access 32 lanes at
+a time; an access is free of bank conflicts when, within every such lane
+group, the lanes touch pairwise distinct 16-byte (resp. 8-byte) bank slots.
+"""
+
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "mla_latent_cache_decode_amd", "csrc", "decode_common.h")
+ROW_BF16 = 1152            # bytes of one bf16 cache row
+D = 576
+CHUNKS = D // 8            # 72 chunks of 8 halves per row
+TILE = 64 * D * 2          # 73728 bytes
+
+
+def _body(name):
+    text = open(HEADER).read()
+    m = re.search(r"__device__ __forceinline__ int " + name + r"\(int t(?:, int c)?\) \{\s*return (.*?);\s*\}",
+                  text, flags=re.S)
+    assert m, f"{name}() not found in {HEADER}"
+    return m.group(1)
+
+
+_SW = _body("sw")
+_TILE_OFF = _body("tile_off")
+
+
+def sw(t):
+    return eval(_SW, {}, {"t": t})
+
+
+def tile_off(t, c):
+    return eval(_TILE_OFF, {"sw": sw}, {"t": t, "c": c})
+
+
+def _conflict_free(addrs, group, slot):
+    for g in range(0, len(addrs), group):
+        slots = [(a // slot) % (256 // slot) for a in addrs[g:g + group]]
+        if len(set(slots)) != len(slots):
+            return False
+    return True
+
+
+def test_layout_is_a_bijection_onto_the_tile():
+    offs = sorted(tile_off(t, c) for t in range(64) for c in range(CHUNKS))
+    assert offs == list(range(0, TILE, 16))
+
+
+def test_tokens_32_apart_are_4096_bytes_apart():
+    # the second 32-token block of a tile is read at +4096
+    for t in range(32):
+        for c in range(CHUNKS):
+            assert tile_off(t + 32, c) == tile_off(t, c) + 4096
+
+
+def test_direct_to_lds_page_loads_write_their_own_chunks():
+    # bf16 kernel, page-block size 64: load k of wave w is piece pn = 18w + k
+    # (token group pn & 7, column block pn >> 3); lane i fetches the row
+    # chunk ((i & 7) ^ sw(i >> 3)) of token 8 (pn & 7) + (i >> 3), flipped
+    # by the low bit of k, and the load writes LDS bytes pn * 1024 + 16 i
+    for wave in range(4):
+        for k in range(18):
+            pn = 18 * wave + k
+            for i in range(64):
+                src = (i >> 3) * ROW_BF16 + ((((i & 7) ^ sw(i >> 3)) << 4) ^ ((k & 1) << 4)) \
+                    + (pn & 7) * 8 * ROW_BF16 + ((pn >> 3) << 7)
+                t, byte = divmod(src, ROW_BF16)
+                assert byte % 16 == 0
+                assert tile_off(t, byte // 16) == pn * 1024 + 16 * i
+
+
+@pytest.mark.parametrize("blk", [0, 1])
+def test_qk_fragment_reads_are_conflict_free(blk):
+    # k-step ks: lane l reads token (l & 31) + 32 blk, chunk 2 (ks & 3) + (l >> 5)
+    # of column block ks >> 2
+    for ks in range(D // 16):
+        addrs = [tile_off(l & 31, 2 * (ks & 3) + (l >> 5)) + (ks >> 2) * 8192 + blk * 4096 for l in range(64)]
+        for l, a in enumerate(addrs):
+            assert a == tile_off((l & 31) + 32 * blk, 8 * (ks >> 2) + 2 * (ks & 3) + (l >> 5))
+        assert _conflict_free(addrs, 16, 16), ks
+
+
+def test_dequantised_piece_stores_are_conflict_free():
+    # fp8 / fp4 piece k of wave w: lane i stores token 16w + (i & 15), chunks
+    # 2 (4k + (i >> 4)) + c (c = 0, 1, one 128-bit store each)
+    for wave in range(4):
+        for k in range(9):
+            for c in range(2):
+                addrs = []
+                for i in range(64):
+                    t = 16 * wave + (i & 15)
+                    a = (tile_off(t, 2 * (i >> 4)) ^ (c << 4)) + k * 8192
+                    assert a == tile_off(t, 2 * (4 * k + (i >> 4)) + c)
+                    addrs.append(a)
+                assert _conflict_free(addrs, 16, 16)
+    # together the pieces cover every chunk of the tile once
+    seen = set()
+    for wave in range(4):
+        for k in range(9):
+            for c in range(2):
+                for i in range(64):
+                    seen.add(tile_off(16 * wave + (i & 15), 2 * (4 * k + (i >> 4)) + c))
+    assert len(seen) == 64 * CHUNKS
+
+
+def _v_lane_addr(lane, m, e):
+    # the V^T fragment pointers of P.V: tokens 4 (g >> 1) + (li >> 2) (+ 8 e),
+    # dims 16 (g & 1) + 4 (li & 3) of a 32-dim block m; e = 1 adds 8 tokens,
+    # which flips the swizzle's low slot bit (address ^ 16)
+    g, li = lane >> 4, lane & 15
+    tok = ((g >> 1) << 2) + (li >> 2)
+    dim = ((g & 1) << 4) + ((li & 3) << 2)
+    off = tile_off(tok, (m * 32 + dim) >> 3) + (dim & 7) * 2
+    return off if e == 0 else (off ^ 16) + 8 * 128
+
+
+def test_transposed_v_reads_address_the_right_elements_without_conflicts():
+    # a P.V step of token step ts and 32-dim block md reads, per lane, 4
+    # consecutive dims of one token at _v_lane_addr + (md >> 1) * 8192 + ts * 2048
+    for ts in range(4):
+        for md in range(16):
+            for e in range(2):
+                addrs = []
+                for lane in range(64):
+                    a = _v_lane_addr(lane, md & 1, e) + (md >> 1) * 8192 + ts * 16 * 128
+                    g, li = lane >> 4, lane & 15
+                    tok = 16 * ts + 8 * e + ((g >> 1) << 2) + (li >> 2)
+                    dim = 32 * md + ((g & 1) << 4) + ((li & 3) << 2)
+                    assert a == tile_off(tok, dim // 8) + (dim % 8) * 2
+                    addrs.append(a)
+                assert _conflict_free(addrs, 32, 8), (ts, md, e)
