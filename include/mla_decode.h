@@ -170,6 +170,31 @@ mla_status_t mla_decode_run(mla_decode_handle_t h,
                             size_t workspace_bytes,
                             void* hip_stream);
 
+/* mla_decode_run_noalloc -- mla_decode_run without a caller workspace, for
+ * callers that cannot allocate device memory at all (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * kernels, same arguments and results as mla_decode_run, minus workspace and
+ * workspace_bytes: the plan and split partials go to a scratch array that the
+ * library keeps in device memory, MLA_NOALLOC_SCRATCH_BYTES per GPU (each GPU
+ * it runs on holds its own copy from the first init on that GPU until the
+ * process ends).  Nothing is allocated per call.
+ *   Returns MLA_ERR_WORKSPACE_TOO_SMALL when mla_decode_workspace_size(h,
+ *   batch) exceeds MLA_NOALLOC_SCRATCH_BYTES (default worker counts fit for
+ *   every n_h * s_q on a 256-CU device; large forced worker counts may not).
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (other streams, other threads) race and give wrong
+ *   results; calls ordered on one stream are safe. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+mla_status_t mla_decode_run_noalloc(mla_decode_handle_t h,
+                                    const void* q,
+                                    const void* kv_pages,
+                                    const int32_t* block_table,
+                                    const int32_t* seq_lens,
+                                    int32_t batch,
+                                    float* out,
+                                    float* lse,
+                                    void* hip_stream);
+
 /* mla_decode_sparse_workspace_size -- device workspace bytes that
  * mla_decode_sparse_run needs for `batch` sequences (0 <= batch <= max_batch)
  * and index lists of `topk` entries (1 <= topk <= 2^20).  `bytes` is a host

@@ -23,4 +23,5 @@ from ._lib import (  # noqa: F401
     MLA_ERR_OUT_OF_MEMORY,
     MLA_FLAG_KV_WITHIN_4GIB,
     KV_WINDOW_BYTES,
+    NOALLOC_SCRATCH_BYTES,
 )

@@ -29,6 +29,8 @@ MLA_ERR_OUT_OF_MEMORY = 5
 # base (include/mla_decode.h): the sparse gathers then use 32-bit offsets
 MLA_FLAG_KV_WITHIN_4GIB = 1
 KV_WINDOW_BYTES = 0xFFFFF000
+# the per-GPU scratch of mla_decode_run_noalloc (include/mla_decode.h)
+NOALLOC_SCRATCH_BYTES = 72 << 20
 
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3_E8M0 = 1
@@ -40,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "mla_decode_init",
     "mla_decode_workspace_size",
     "mla_decode_run",
+    "mla_decode_run_noalloc",
     "mla_decode_sparse_workspace_size",
     "mla_decode_sparse_run",
     "mla_decode_set_profile_events",
@@ -98,6 +101,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mla_decode_workspace_size.restype = ctypes.c_int
     lib.mla_decode_run.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.mla_decode_run.restype = ctypes.c_int
+    lib.mla_decode_run_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.mla_decode_run_noalloc.restype = ctypes.c_int
     lib.mla_decode_sparse_workspace_size.argtypes = [vp, i32, i32, ctypes.POINTER(sz)]
     lib.mla_decode_sparse_workspace_size.restype = ctypes.c_int
     lib.mla_decode_sparse_run.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
@@ -215,6 +220,34 @@ class MlaDecode:
             workspace.numel() * workspace.element_size(), stream)
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_run")
+
+    def run_noalloc(self, q, kv, block_table, seq_lens, out, lse=None, stream=None) -> None:
+        """``run`` through mla_decode_run_noalloc: no workspace, the library's
+        per-GPU scratch instead (calls that overlap on one GPU race)."""
+        import torch
+        p = self.params
+        batch = int(seq_lens.shape[0])
+        _check(q, (batch, p.s_q, p.n_h, p.d_c + p.d_r), torch.bfloat16, "q")
+        _check(out, (batch, p.s_q, p.n_h, p.d_c), torch.float32, "out")
+        if lse is not None:
+            _check(lse, (batch, p.s_q, p.n_h), torch.float32, "lse")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != batch \
+                or block_table.shape[1] != p.max_blocks_per_seq or not block_table.is_contiguous():
+            raise ValueError("block_table must be contiguous int32 [batch, max_blocks_per_seq]")
+        if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens must be contiguous int32 [batch]")
+        if not kv.is_contiguous() or not kv.is_cuda:
+            raise ValueError("kv pages must be a contiguous device tensor")
+        for t in (q, out, block_table, seq_lens) + ((lse,) if lse is not None else ()):
+            if not t.is_cuda:
+                raise ValueError("all tensors must be on the GPU")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = self._lib.mla_decode_run_noalloc(
+            self._h, q.data_ptr(), kv.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), batch,
+            out.data_ptr(), lse.data_ptr() if lse is not None else None, stream)
+        if st != MLA_OK:
+            raise MlaError(st, "mla_decode_run_noalloc")
 
     # -- the sparse (top-k) decode -------------------------------------------
     def sparse_workspace_size(self, batch: int, topk: int) -> int:

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["decode_bf16.hip", "decode.hip", "plan_combine.hip", "api.cpp"]
+SOURCES = ["decode_bf16.hip", "decode.hip", "plan_combine.hip", "scratch.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -27,6 +27,7 @@ struct mla_decode_handle {
     int partial_slots;         // upper bound on partial results
     hipEvent_t ev_start;
     hipEvent_t ev_stop;
+    void* scratch;             // this device's copy of the no-alloc scratch (a device address)
 };
 
 namespace {
@@ -206,6 +207,12 @@ mla_status_t mla_decode_init(const mla_decode_params_t* params, mla_decode_handl
         h->num_workers = w < 1 ? 1 : (w > mla::kMaxWorkers ? mla::kMaxWorkers : w);
     }
     h->partial_slots = h->num_workers > 1 ? 2 * (h->num_workers - 1) : 1;
+    // the device's no-alloc scratch: its address is taken here, once per
+    // device, with the device current
+    if (mla::scratch_address(dev, &h->scratch) != hipSuccess) {
+        delete h;
+        return MLA_ERR_HIP;
+    }
     const char* log = std::getenv("MLA_DECODE_LOG");
     if (log && log[0] == '1') {
         std::fprintf(stderr, "[mla_decode] device %d (%s) CUs=%d rows=%d row_groups=%d workers=%d kv=%s\n",
@@ -287,6 +294,21 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     ca.rows = h->rows;
     if (mla::launch_combine(ca, h->num_workers, stream) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
+}
+
+mla_status_t mla_decode_run_noalloc(mla_decode_handle_t h, const void* q, const void* kv_pages,
+                                    const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                    float* out, float* lse, void* hip_stream) {
+    if (!h) return MLA_ERR_INVALID_ARGUMENT;
+    if (batch < 0 || batch > h->p.max_batch) return MLA_ERR_INVALID_ARGUMENT;
+    if (!h->scratch) return MLA_ERR_HIP;
+    // the plan and partials of this handle and batch must fit the scratch
+    if (layout(h, batch).total > mla::kNoAllocScratchBytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    // the scratch's device address (taken at init), never the array's name;
+    // nothing in it needs clearing: the decode writes every plan record and
+    // partial before the combine reads it
+    return mla_decode_run(h, q, kv_pages, block_table, seq_lens, batch, out, lse, h->scratch,
+                          mla::kNoAllocScratchBytes, hip_stream);
 }
 
 mla_status_t mla_decode_sparse_workspace_size(mla_decode_handle_t h, int32_t batch, int32_t topk, size_t* bytes) {

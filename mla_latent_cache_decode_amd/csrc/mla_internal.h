@@ -111,4 +111,12 @@ hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStre
 // count); it sizes the combine's LDS and picks its shape.
 hipError_t launch_combine(const CombineArgs& a, int max_splits, hipStream_t stream);
 
+// Bytes of the per-device scratch that mla_decode_run_noalloc uses as its
+// workspace (MLA_NOALLOC_SCRATCH_BYTES in the public header).
+constexpr size_t kNoAllocScratchBytes = (size_t)72 << 20;
+// The device address of `device`'s copy of that scratch; `device` must be
+// current.  Taken with hipGetSymbolAddress on the first call per device and
+// kept; later calls return the kept address.  Thread-safe.
+hipError_t scratch_address(int device, void** out);
+
 }  // namespace mla
