@@ -22,10 +22,10 @@ Order of the run, all on one stream:
      Five untimed steps follow, back to the warm state.
   3. The timed region: exactly K steps (--steps) back to back, warm cache,
      bracketed by synchronisations: ``value`` and ``ms_per_step``.
-  4. A sampling pass of --kernel-samples more steps whose decode kernel is
-     timed by HIP events recorded with its own dispatch (these cost ~6 us a
-     step, so the timed region runs without them): the dominant kernel's
-     roofline.
+  4. A sampling pass of 8 x --kernel-samples more steps, every 8th of whose
+     decode kernels is timed by HIP events recorded with its own dispatch
+     (these cost ~6 us a step, so the timed region runs without them): the
+     dominant kernel's roofline.
 
 Prints one JSON line: KV-read GB/s (whole job), TFLOP/s, the cold-cache
 figures, the dominant kernel's roofline and the float64 CPU oracle timed on a
@@ -220,6 +220,8 @@ def main():
             flush_w.fill_(k & 0xFF)
             torch.sum(flush_r, dim=0, out=sink)
             s0, s1, k0, k1 = ev(), ev(), ev(), ev()
+            k0.record(stream)   # torch only reads events it has seen recorded
+            k1.record(stream)
             lib.mla_decode_set_profile_events(dec._h, k0.cuda_event, k1.cuda_event)
             s0.record(stream)
             step()
@@ -245,7 +247,9 @@ def main():
     ms_total = t_start.elapsed_time(t_stop)
     ms_step = ms_total / args.steps
 
-    # sampling pass: the decode kernel's own dispatch timestamps, every step
+    # sampling pass: the decode kernel's own dispatch timestamps on every
+    # 8th step (events on consecutive steps slow the steps down), bare steps
+    # in between
     n_samp = max(args.kernel_samples, 10)
     samp = [(ev(), ev()) for _ in range(n_samp)]
     for a, b in samp:           # torch only reads events it has seen recorded
@@ -255,7 +259,9 @@ def main():
     for a, b in samp:
         lib.mla_decode_set_profile_events(dec._h, a.cuda_event, b.cuda_event)
         step()
-    lib.mla_decode_set_profile_events(dec._h, None, None)
+        lib.mla_decode_set_profile_events(dec._h, None, None)
+        for _ in range(7):
+            step()
     torch.cuda.synchronize()
     kernel_ms = [a.elapsed_time(b) for a, b in samp]
     kms = float(np.mean(kernel_ms))

@@ -19,6 +19,8 @@ LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["decode_bf16.hip", "decode.hip", "plan_combine.hip", "scratch.hip", "api.cpp"]
 
+# per-source extra compiler flags
+SOURCE_FLAGS: dict = {}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -56,7 +58,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([HIPCC] + flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + flags + SOURCE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     # the translation units compile independently: one hipcc each, in parallel
     jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1)))

@@ -57,29 +57,11 @@ constexpr int kQkSteps = 2 * kKSteps;               // 72: two 32-token blocks x
 
 static_assert(4 * kDmaPerWave * 1024 == kTileBytes, "four waves move a page");
 
-// One 1 KiB direct-to-LDS load: lane i's 16 bytes at buffer offset voff land
-// at LDS address dst + 16 i.  Issued as asm: the compiler cannot tell that it
-// does not alias the tile being read and would otherwise wait for it
-// (vmcnt(0)) before every LDS read.  Completion is waited for explicitly.
-// The cache is streamed once per workgroup: non-temporal (nt) loads keep it
-// from displacing other data in the caches (measured -3.5 % on the long
-// context workload).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, uint32_t dst) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r), "{m0}"(dst) : "memory");
-}
-
 // The same 1 KiB direct-to-LDS load with a 64-bit address per lane (the
 // sparse gather: every token row can sit anywhere in the cache).  No
 // instruction offset: it would move the LDS destination as well.
 __device__ __forceinline__ void dma16_gather(uint64_t addr, uint32_t dst) {
     asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(addr), "{m0}"(dst) : "memory");
-}
-
-// bf16 pair -> fp16 pair (round to nearest even; exact inside the fp16 range)
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t d) {
-    const float lo = __builtin_bit_cast(float, d << 16);
-    const float hi = __builtin_bit_cast(float, d & 0xFFFF0000u);
-    return __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
 }
 
 // S^T += K Q^T on one k-step, with the accumulator in arch VGPRs.  Issued as

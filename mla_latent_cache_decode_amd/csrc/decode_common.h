@@ -123,6 +123,24 @@ __device__ __forceinline__ int pinned(int v) {
     return v;
 }
 
+// One 1 KiB direct-to-LDS load: lane i's 16 bytes at buffer offset voff land
+// at LDS address dst + 16 i.  Issued as asm: the compiler cannot tell that it
+// does not alias the tile being read and would otherwise wait for it
+// (vmcnt(0)) before every LDS read.  Completion is waited for explicitly.
+// The cache is streamed once per workgroup: non-temporal (nt) loads keep it
+// from displacing other data in the caches (measured -3.5 % on the long
+// context workload).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, uint32_t dst) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r), "{m0}"(dst) : "memory");
+}
+
+// bf16 pair -> fp16 pair (round to nearest even; exact inside the fp16 range)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t d) {
+    const float lo = __builtin_bit_cast(float, d << 16);
+    const float hi = __builtin_bit_cast(float, d & 0xFFFF0000u);
+    return __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
+}
+
 // ---------------------------------------------------------------------------
 // work plan
 // ---------------------------------------------------------------------------
@@ -136,7 +154,8 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
-// Exclusive scan of two ints over the 256 threads, with the totals.
+// Exclusive scan of two ints over the NT threads of the block, with the totals.
+template <int NT>
 __device__ __forceinline__ void block_scan2(int& a, int& b, int& ta, int& tb, int* sbuf, int tid) {
     const int lane = tid & 63, wave = tid >> 6;
     const int ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
@@ -149,7 +168,7 @@ __device__ __forceinline__ void block_scan2(int& a, int& b, int& ta, int& tb, in
     int pa = 0, pb = 0;
     ta = tb = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         if (w < wave) {
             pa += sbuf[w * 2 + 0];
             pb += sbuf[w * 2 + 1];
@@ -223,18 +242,21 @@ __device__ WorkerStart plan_worker_wave(const DecodeArgs& a, int worker, bool wr
     return ws;
 }
 
+// NT: threads of the block (a multiple of 64, at most 512; sbuf holds 32 ints)
+template <int NT = kDecodeThreads>
 __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_info, int* sbuf, int tid) {
+    static_assert(NT % 64 == 0 && NT <= 512, "block of whole waves, at most 8");
     if (a.batch <= 64) return plan_worker_wave(a, worker, write_info, tid);
     const int B = a.batch, G = a.num_workers, c = a.overhead_units;
     int t_cost = 0;
     const int my_len = tid < B ? plan_len(a, tid) : 0;      // reused by the first chunk
     {
         int local = my_len > 0 ? (my_len + kPage - 1) / kPage + c : 0, zero = 0, tz;
-        for (int b = tid + kDecodeThreads; b < B; b += kDecodeThreads) {
+        for (int b = tid + NT; b < B; b += NT) {
             const int L = plan_len(a, b);
             local += L > 0 ? (L + kPage - 1) / kPage + c : 0;
         }
-        block_scan2(local, zero, t_cost, tz, sbuf, tid);
+        block_scan2<NT>(local, zero, t_cost, tz, sbuf, tid);
     }
     const int64_t Q = max(max(((int64_t)t_cost + G - 1) / G, (int64_t)a.min_quota), (int64_t)1);
     const int64_t w_lo = (int64_t)worker * Q, w_hi = w_lo + Q;
@@ -246,7 +268,7 @@ __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_i
     ws.quota = Q;
     int64_t carry_cost = 0;
     int carry_slot = 0;
-    for (int base = 0; base < B; base += kDecodeThreads) {
+    for (int base = 0; base < B; base += NT) {
         const int b = base + tid;
         int pages = 0;
         if (b < B) {
@@ -255,12 +277,12 @@ __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_i
         }
         // a sequence's segment count depends on its cost prefix, so two scans
         int cost_ex = pages > 0 ? pages + c : 0, zero = 0, tc, tz;
-        block_scan2(cost_ex, zero, tc, tz, sbuf, tid);
+        block_scan2<NT>(cost_ex, zero, tc, tz, sbuf, tid);
         const int64_t C = carry_cost + cost_ex;
         const int64_t A = C + c, E = A + pages;
         const int n = pages > 0 ? (int)((E - 1) / Q - A / Q + 1) : 0;
         int slot_ex = n > 1 ? n : 0, zero2 = 0, ts, tz2;
-        block_scan2(slot_ex, zero2, ts, tz2, sbuf, tid);
+        block_scan2<NT>(slot_ex, zero2, ts, tz2, sbuf, tid);
         const int slot = carry_slot + slot_ex;
         if (write_info && b < B) {
             const int64_t owner = pages > 0 ? A / Q : min(C / Q, (int64_t)G - 1);
@@ -274,22 +296,22 @@ __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_i
             const bool cand = b < B && pages > 0 && E > w_lo;
             const unsigned long long m = __builtin_amdgcn_ballot_w64(cand);
             __syncthreads();
-            if ((tid & 63) == 0) sbuf[8 + (tid >> 6)] = m ? (int)__builtin_ctzll(m) + (tid & ~63) : kDecodeThreads;
+            if ((tid & 63) == 0) sbuf[16 + (tid >> 6)] = m ? (int)__builtin_ctzll(m) + (tid & ~63) : NT;
             __syncthreads();
-            int first = kDecodeThreads;
+            int first = NT;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) first = min(first, sbuf[8 + w]);
-            if (first < kDecodeThreads) {
+            for (int w = 0; w < NT / 64; ++w) first = min(first, sbuf[16 + w]);
+            if (first < NT) {
                 __syncthreads();
                 if (tid == first) {
-                    sbuf[12] = (int)(C & 0x3FFFFFFF);
-                    sbuf[13] = (int)(C >> 30);
-                    sbuf[14] = slot;
+                    sbuf[24] = (int)(C & 0x3FFFFFFF);
+                    sbuf[25] = (int)(C >> 30);
+                    sbuf[26] = slot;
                 }
                 __syncthreads();
                 ws.b = base + first;
-                ws.cost = ((int64_t)sbuf[13] << 30) | (int64_t)sbuf[12];
-                ws.slot = sbuf[14];
+                ws.cost = ((int64_t)sbuf[25] << 30) | (int64_t)sbuf[24];
+                ws.slot = sbuf[26];
             }
         }
         carry_cost += tc;
@@ -313,12 +335,12 @@ __device__ WorkerStart plan_worker(const DecodeArgs& a, int worker, bool write_i
 // them only (kWavesPerRange waves per page), so a wave still needs a single
 // block-table entry and a single buffer descriptor per tile.  When PS >= 64
 // a tile lies inside one page, at row (p * 64) % PS.
-template <int PS>
+template <int PS, int NW = kDecodeThreads / 64>
 struct PageGeom {
     static_assert(PS >= 16 && PS <= 256 && (PS & (PS - 1)) == 0, "page block: a power of two in 16 .. 256");
     static constexpr int kRanges = PS < kPage ? kPage / PS : 1;
     static constexpr int kRangeTok = kPage / kRanges;
-    static constexpr int kWavesPerRange = (kDecodeThreads / 64) / kRanges;
+    static constexpr int kWavesPerRange = NW / kRanges;
     static_assert(kWavesPerRange >= 1, "every page of a tile needs a wave");
     // first token (within a tile) of the pages wave w loads from
     __device__ static constexpr int tok0(int wave) { return kRanges == 1 ? 0 : (wave / kWavesPerRange) * kRangeTok; }
@@ -362,15 +384,18 @@ __device__ __forceinline__ void store_partial4(uint16_t* dst, f32x4 v) {
 }
 
 // Workgroups are dealt to the 8 XCDs round robin (block i on XCD i % 8).
-// When the worker count G is a multiple of 8 the row groups of one worker
-// are given blocks on the same XCD, so they read each page through the same
-// L2 at about the same time and the cache is fetched from HBM once.
+// When the worker count G is a multiple of 8, XCD x serves workers
+// x * G/8 .. (x + 1) * G/8 - 1, all row groups of each: consecutive workers,
+// which the cost-axis plan gives adjacent splits of one sequence, then share
+// an L2 and fetch that sequence's queries from HBM once per XCD, and the row
+// groups of one worker read each page through the same L2 at about the same
+// time, so the cache is fetched from HBM once.
 __device__ __forceinline__ void block_role(int G, int& worker, int& rg) {
     if (G % 8 == 0) {
         const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
         const int R = (int)gridDim.x / G;
         rg = j % R;
-        worker = (j / R) * 8 + xcd;
+        worker = xcd * (G / 8) + j / R;
     } else {
         worker = blockIdx.x % G;
         rg = blockIdx.x / G;
@@ -380,13 +405,13 @@ __device__ __forceinline__ void block_role(int G, int& worker, int& rg) {
 // Launch a decode kernel: with profile events, through the dispatch that
 // records its own start and end timestamps into them; otherwise a plain
 // launch (what a captured HIP graph then holds).
-template <typename Kernel>
+template <int NT = kDecodeThreads, typename Kernel>
 hipError_t launch_with_events(Kernel kernel, dim3 grid, hipStream_t stream, hipEvent_t ev_start,
                               hipEvent_t ev_stop, const DecodeArgs& a) {
     if (ev_start && ev_stop)
-        hipExtLaunchKernelGGL(kernel, grid, dim3(kDecodeThreads), 0, stream, ev_start, ev_stop, 0, a);
+        hipExtLaunchKernelGGL(kernel, grid, dim3(NT), 0, stream, ev_start, ev_stop, 0, a);
     else
-        hipLaunchKernelGGL(kernel, grid, dim3(kDecodeThreads), 0, stream, a);
+        hipLaunchKernelGGL(kernel, grid, dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -7,6 +7,10 @@ Two modes:
            calls, and (with --last N) the average over each kernel's last N
            dispatches from the kernel trace: the timed steps of a bench run,
            after its warm-up.
+  counters from one or more ``rocprofv3 --pmc`` runs: per-dispatch averages
+           of each counter of one kernel, and derived figures (the clock the
+           dispatches ran at, matrix-core busy fraction, MFMA rate, LDS bank
+           conflicts per LDS-active cycle).
   traffic  from two ``rocprofv3 --pmc`` runs (FETCH_SIZE, then WRITE_SIZE;
            both in KiB per dispatch) of ``bench.py --copy-mb N``: the HBM
            bytes per dispatch of one kernel, each counter scaled by what it
@@ -153,6 +157,55 @@ def _traffic(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+def _counters(args) -> str:
+    """Per-dispatch averages of every counter of one kernel over one or more
+    ``--pmc`` runs (one CSV each), plus the clock the dispatches ran at when
+    GRBM_GUI_ACTIVE (GPU clock cycles) and the dispatch timestamps are there."""
+    lines = [f"kernel: {args.kernel}", f"workload: {args.workload}",
+             f"source_hash: {kernel_source_hash(args.kernel) if args.kernel in KERNEL_SOURCES else '-'}", ""]
+    vals: dict[str, float] = {}
+    for path, cmd in zip(args.csv, args.command):
+        per: dict[str, list[float]] = {}
+        dur_by_dispatch: dict[str, int] = {}
+        for r in csv.DictReader(open(path)):
+            if _short(r["Kernel_Name"]).split("<")[0].split("::")[-1] != args.kernel:
+                continue
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                dur_by_dispatch[r.get("Dispatch_Id", str(len(dur_by_dispatch)))] = \
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        durs = list(dur_by_dispatch.values())
+        if not per:
+            sys.exit(f"no {args.kernel} dispatch in {path}")
+        n = min(len(v) for v in per.values())
+        last = args.last or n
+        lines.append(f"command: {cmd}")
+        lines.append(f"  dispatches: {n} (averaged over the last {min(last, n)})")
+        for name in sorted(per):
+            v = statistics.mean(per[name][-last:])
+            vals[name] = v
+            lines.append(f"  {name:<36} {v:>20.1f}")
+        if durs:
+            d = statistics.mean(durs[-last:])
+            vals["_duration_ns"] = d
+            lines.append(f"  {'dispatch duration (ns)':<36} {d:>20.1f}")
+        lines.append("")
+    lines.append("derived:")
+    if "GRBM_GUI_ACTIVE" in vals and "_duration_ns" in vals:
+        lines.append(f"  GPU clock over the dispatch = GRBM_GUI_ACTIVE / duration = "
+                     f"{vals['GRBM_GUI_ACTIVE'] / vals['_duration_ns'] * 1e3:.0f} MHz")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals:
+        u = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (vals["GRBM_GUI_ACTIVE"] * args.cus * 4)
+        lines.append(f"  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {args.cus} CUs x 4 SIMDs) = {u:.3f}")
+    for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16"):
+        if k in vals and "_duration_ns" in vals:
+            lines.append(f"  {k} x 512 flop / duration = {vals[k] * 512 / vals['_duration_ns'] / 1e3:.1f} TFLOP/s")
+    if "SQ_LDS_BANK_CONFLICT" in vals and "SQ_LDS_IDX_ACTIVE" in vals and vals["SQ_LDS_IDX_ACTIVE"]:
+        lines.append(f"  LDS bank-conflict cycles / LDS active cycles = "
+                     f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_LDS_IDX_ACTIVE']:.4f}")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -170,8 +223,16 @@ def main(argv=None):
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", required=True, action="append", help="one per --pmc run")
+    c.add_argument("--command", required=True, action="append", help="one per --pmc run, same order")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--last", type=int, default=0, help="average the last N dispatches (0: all)")
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--out", required=True)
     args = ap.parse_args(argv)
-    text = _stats(args) if args.mode == "stats" else _traffic(args)
+    text = {"stats": _stats, "traffic": _traffic, "counters": _counters}[args.mode](args)
     with open(args.out, "w") as f:
         f.write(text)
     print(text, end="")
