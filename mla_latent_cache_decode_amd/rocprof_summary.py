@@ -102,12 +102,15 @@ def _stats(args) -> str:
         for r in csv.DictReader(open(trace)):
             per.setdefault(r["Kernel_Name"], []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        lines += ["", f"last {args.last} dispatches of each kernel (the timed steps):",
+        skip = args.skip_last
+        what = f"dispatches -{args.last + skip} .. -{skip + 1} of each kernel" if skip else \
+            f"last {args.last} dispatches of each kernel"
+        lines += ["", f"{what} ({args.label}):",
                   f"{'kernel':<60} {'n':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}"]
         for name, ds in per.items():
-            d = ds[-args.last:]
-            if len(ds) < args.last:
+            if len(ds) < args.last + skip:
                 continue
+            d = ds[len(ds) - skip - args.last:len(ds) - skip]
             lines.append(f"{_short(name):<60} {len(d):>6} {statistics.mean(d):>10.2f} {min(d):>10.2f} {max(d):>10.2f}")
     return "\n".join(lines) + "\n"
 
@@ -190,19 +193,25 @@ def _counters(args) -> str:
             vals["_duration_ns"] = d
             lines.append(f"  {'dispatch duration (ns)':<36} {d:>20.1f}")
         lines.append("")
-    lines.append("derived:")
+    lines.append("derived (GRBM_GUI_ACTIVE counts GPU clock cycles summed over the XCDs):")
     if "GRBM_GUI_ACTIVE" in vals and "_duration_ns" in vals:
-        lines.append(f"  GPU clock over the dispatch = GRBM_GUI_ACTIVE / duration = "
-                     f"{vals['GRBM_GUI_ACTIVE'] / vals['_duration_ns'] * 1e3:.0f} MHz")
+        cyc = vals["GRBM_GUI_ACTIVE"] / args.xcds
+        lines.append(f"  GPU clock over the dispatch = GRBM_GUI_ACTIVE / {args.xcds} / duration = "
+                     f"{cyc / vals['_duration_ns'] * 1e3:.0f} MHz")
     if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals:
-        u = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (vals["GRBM_GUI_ACTIVE"] * args.cus * 4)
-        lines.append(f"  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {args.cus} CUs x 4 SIMDs) = {u:.3f}")
-    for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16"):
-        if k in vals and "_duration_ns" in vals:
-            lines.append(f"  {k} x 512 flop / duration = {vals[k] * 512 / vals['_duration_ns'] / 1e3:.1f} TFLOP/s")
+        simd_cycles = vals["GRBM_GUI_ACTIVE"] / args.xcds * args.cus * 4
+        lines.append(f"  matrix cores busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {args.xcds} x {args.cus} CUs "
+                     f"x 4 SIMDs) = {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.3f}")
+    mops = sum(vals.get(k, 0.0) for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16"))
+    if mops and "_duration_ns" in vals:
+        lines.append(f"  MFMA work = (MOPS_BF16 + MOPS_F16) x 512 flop = {mops * 512 / 1e9:.2f} GFLOP per dispatch; "
+                     f"over the dispatch duration {mops * 512 / vals['_duration_ns'] / 1e3:.1f} TFLOP/s")
     if "SQ_LDS_BANK_CONFLICT" in vals and "SQ_LDS_IDX_ACTIVE" in vals and vals["SQ_LDS_IDX_ACTIVE"]:
         lines.append(f"  LDS bank-conflict cycles / LDS active cycles = "
                      f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_LDS_IDX_ACTIVE']:.4f}")
+    if "TCP_TCC_READ_REQ_LATENCY" in vals and vals.get("TCP_TCC_READ_REQ"):
+        lines.append(f"  mean L1 -> L2 read latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ = "
+                     f"{vals['TCP_TCC_READ_REQ_LATENCY'] / vals['TCP_TCC_READ_REQ']:.0f} cycles")
     return "\n".join(lines) + "\n"
 
 
@@ -214,6 +223,8 @@ def main(argv=None):
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--last", type=int, default=0, help="also average the last N dispatches per kernel")
+    s.add_argument("--skip-last", type=int, default=0, help="... leaving out the final M dispatches")
+    s.add_argument("--label", default="the timed steps")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -230,6 +241,7 @@ def main(argv=None):
     c.add_argument("--workload", required=True)
     c.add_argument("--last", type=int, default=0, help="average the last N dispatches (0: all)")
     c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
     c.add_argument("--out", required=True)
     args = ap.parse_args(argv)
     text = {"stats": _stats, "traffic": _traffic, "counters": _counters}[args.mode](args)
