@@ -292,7 +292,7 @@ def main():
                 "frac": round(k_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
     info = dec.info()
     from mla_latent_cache_decode_amd.rocprof_summary import kernel_for_dtype
-    kernel = kernel_for_dtype(s.kv_dtype)
+    kernel = kernel_for_dtype(s.kv_dtype, sparse)
     traffic = measured_traffic(kernel, s.name)
     res = {
         "metric": "MLA decode KV-read GB/s (% of HBM peak) + TFLOP/s, n_h=128, 1 GPU",

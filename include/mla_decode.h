@@ -112,7 +112,8 @@ mla_status_t mla_decode_init(const mla_decode_params_t* params, mla_decode_handl
 /* mla_decode_workspace_size -- device workspace bytes that mla_decode_run needs
  * for `batch` sequences (0 <= batch <= max_batch).  `bytes` is a host pointer.
  * The workspace holds the per-call work plan and the split-KV partial results
- * (fp16 normalised outputs and fp32 LSEs of every context split). */
+ * (fp16 normalised outputs and fp32 LSEs of every context split); for the FP8
+ * cache also the queries as two e4m3 terms (1216 bytes per query row). */
 mla_status_t mla_decode_workspace_size(mla_decode_handle_t h, int32_t batch, size_t* bytes);
 
 /* mla_decode_run -- one decode step for `batch` sequences, all heads, all queries.
@@ -142,9 +143,13 @@ mla_status_t mla_decode_workspace_size(mla_decode_handle_t h, int32_t batch, siz
  * Tail slots after a sequence's last token, unused pages and row padding are
  * never read, whatever they hold.
  *
- * Value range (precondition).  The products run on 16-bit matrix cores with
- * fp32 accumulation: bf16 cache values enter Q.K^T as they are, but P.V (and,
- * for the quantised formats, both products) takes them converted to fp16.
+ * Value range (precondition).  The products run on matrix cores with fp32
+ * accumulation.  BF16 cache: Q.K^T takes the values as they are (bf16 MFMA).
+ * FP8 cache: Q.K^T multiplies the cache's own e4m3 codes and e8m0 scales by
+ * the query split into two e4m3 terms with one e8m0 scale per 32
+ * (q ~ q_hi + q_lo, q_lo encoding the residual; block-scaled fp8 MFMA).
+ * FP4 cache: Q.K^T takes the dequantised values converted to fp16.  P.V takes
+ * the dequantised (bf16: the raw) values converted to fp16 for every format.
  * Every decoded cache element x of a visible token must therefore satisfy
  * |x| < 65520 (every finite bf16 value up to 65280 in magnitude; an fp8 code
  * times its scale up to 61440); a larger one becomes infinite and the output
@@ -179,12 +184,16 @@ mla_status_t mla_decode_run(mla_decode_handle_t h,
  * it runs on holds its own copy from the first init on that GPU until the
  * process ends).  Nothing is allocated per call.
  *   Returns MLA_ERR_WORKSPACE_TOO_SMALL when mla_decode_workspace_size(h,
- *   batch) exceeds MLA_NOALLOC_SCRATCH_BYTES (default worker counts fit for
- *   every n_h * s_q on a 256-CU device; large forced worker counts may not).
+ *   batch) exceeds MLA_NOALLOC_SCRATCH_BYTES.  With the default worker count
+ *   on a 256-CU device the plan and partials take under 68 MB for every
+ *   n_h * s_q, so bf16 and fp4 calls always fit; the FP8 cache adds its
+ *   two-term query rows (batch * s_q * n_h * 1216 bytes), which fit up to
+ *   about 400 sequences at n_h = 128, s_q = 1.  Large forced worker counts
+ *   may not fit.
  *   Every call on one GPU shares that GPU's scratch: calls that overlap in
  *   time on one GPU (other streams, other threads) race and give wrong
  *   results; calls ordered on one stream are safe. */
-#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 mla_status_t mla_decode_run_noalloc(mla_decode_handle_t h,
                                     const void* q,
                                     const void* kv_pages,
@@ -199,8 +208,9 @@ mla_status_t mla_decode_run_noalloc(mla_decode_handle_t h,
  * mla_decode_sparse_run needs for `batch` sequences (0 <= batch <= max_batch)
  * and index lists of `topk` entries (1 <= topk <= 2^20).  `bytes` is a host
  * pointer.  The workspace holds the work plan and split partials of
- * batch * s_q query units; its size does not depend on topk (the decode
- * reads the index lists itself, nothing per entry is stored). */
+ * batch * s_q query units (and, for the FP8 cache, their two-term query
+ * rows); its size does not depend on topk (the decode reads the index lists
+ * itself, nothing per entry is stored). */
 mla_status_t mla_decode_sparse_workspace_size(mla_decode_handle_t h, int32_t batch, int32_t topk,
                                               size_t* bytes);
 

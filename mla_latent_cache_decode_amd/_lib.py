@@ -30,7 +30,7 @@ MLA_ERR_OUT_OF_MEMORY = 5
 MLA_FLAG_KV_WITHIN_4GIB = 1
 KV_WINDOW_BYTES = 0xFFFFF000
 # the per-GPU scratch of mla_decode_run_noalloc (include/mla_decode.h)
-NOALLOC_SCRATCH_BYTES = 72 << 20
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3_E8M0 = 1

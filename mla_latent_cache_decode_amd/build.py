@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["decode_bf16.hip", "decode.hip", "plan_combine.hip", "scratch.hip", "api.cpp"]
+SOURCES = ["decode_bf16.hip", "decode.hip", "decode_mx.hip", "plan_combine.hip", "scratch.hip", "api.cpp"]
 
 # per-source extra compiler flags
 SOURCE_FLAGS: dict = {}

@@ -32,6 +32,8 @@ struct mla_decode_handle {
 
 namespace {
 
+static_assert(MLA_NOALLOC_SCRATCH_BYTES == mla::kNoAllocScratchBytes, "the header states the scratch size");
+
 constexpr size_t kAlign = 256;
 constexpr int kOverheadUnits = 3;    // per-segment cost (query load, first page, epilogue), in pages: measured ~2.2 tiles of prologue plus the partial write
 constexpr int kMinQuota = 1;
@@ -39,7 +41,7 @@ constexpr int kMinQuota = 1;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-    size_t seq_nsplit, seq_slot, part_lse, part_o, total;
+    size_t seq_nsplit, seq_slot, part_lse, part_o, qx, total;
 };
 
 WsLayout layout(const mla_decode_handle* h, int32_t batch) {
@@ -50,6 +52,9 @@ WsLayout layout(const mla_decode_handle* h, int32_t batch) {
     l.seq_slot = off;      off += align_up(nb * sizeof(int32_t));
     l.part_lse = off;      off += align_up((size_t)h->partial_slots * h->rows * sizeof(float));
     l.part_o = off;        off += align_up((size_t)h->partial_slots * h->rows * mla::kDc * sizeof(uint16_t));
+    // fp8 cache: the queries as two e4m3 terms, written by the decode's first kernel
+    l.qx = off;
+    if (h->p.kv_dtype == MLA_KV_FP8_E4M3_E8M0) off += align_up(nb * (size_t)h->rows * mla::kMxQxRowBytes);
     l.total = off;
     return l;
 }
@@ -61,7 +66,7 @@ constexpr int32_t kMaxTopk = 1 << 20;
 // Workspace of a sparse run: the plan and partials of batch * s_q units of
 // n_h rows.
 struct SparseLayout {
-    size_t seq_nsplit, seq_slot, part_lse, part_o, total;
+    size_t seq_nsplit, seq_slot, part_lse, part_o, qx, total;
     int units, tiles, row_groups, workers, slots;
 };
 
@@ -85,6 +90,8 @@ SparseLayout sparse_layout(const mla_decode_handle* h, int32_t batch, int32_t to
     l.seq_slot = off;    off += align_up(nu * sizeof(int32_t));
     l.part_lse = off;    off += align_up((size_t)l.slots * h->p.n_h * sizeof(float));
     l.part_o = off;      off += align_up((size_t)l.slots * h->p.n_h * mla::kDc * sizeof(uint16_t));
+    l.qx = off;
+    if (h->p.kv_dtype == MLA_KV_FP8_E4M3_E8M0) off += align_up(nu * (size_t)h->p.n_h * mla::kMxQxRowBytes);
     l.total = off;
     return l;
 }
@@ -111,6 +118,7 @@ mla::DecodeArgs decode_args(const mla_decode_handle* h, const void* q, const voi
     da.out = out;
     da.lse = lse;
     da.plan = plan;
+    da.qx = nullptr;
     da.page_bytes = (int64_t)h->p.block_size * (int64_t)mla_kv_row_stride(h->p.kv_dtype, h->p.d_c, h->p.d_r);
     da.page_size = h->p.block_size;
     da.n_h = h->p.n_h;
@@ -280,10 +288,16 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     // profile events (both or neither) take the decode kernel's own timestamps
     const hipEvent_t e0 = h->ev_start && h->ev_stop ? h->ev_start : nullptr;
     const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
-    const hipError_t e =
-        h->p.kv_dtype == MLA_KV_BF16
-            ? mla::launch_decode_bf16(da, h->row_groups, stream, e0, e1)
-            : mla::launch_decode_fp8(da, h->row_groups, stream, e0, e1, h->p.kv_dtype == MLA_KV_FP4_E2M1_E8M0);
+    hipError_t e = hipSuccess;
+    if (h->p.kv_dtype == MLA_KV_BF16) {
+        e = mla::launch_decode_bf16(da, h->row_groups, stream, e0, e1);
+    } else if (h->p.kv_dtype == MLA_KV_FP8_E4M3_E8M0) {
+        da.qx = ws + l.qx;
+        e = mla::launch_quantize_q_mx(da, stream);
+        if (e == hipSuccess) e = mla::launch_decode_fp8_mx(da, h->row_groups, stream, e0, e1);
+    } else {
+        e = mla::launch_decode_fp4(da, h->row_groups, stream, e0, e1);
+    }
     if (e != hipSuccess) return MLA_ERR_HIP;
 
     mla::CombineArgs ca{};
@@ -352,10 +366,16 @@ mla_status_t mla_decode_sparse_run(mla_decode_handle_t h, const void* q, const v
     const hipEvent_t e0 = h->ev_start && h->ev_stop ? h->ev_start : nullptr;
     const hipEvent_t e1 = e0 ? h->ev_stop : nullptr;
     const bool window = (h->p.flags & MLA_FLAG_KV_WITHIN_4GIB) != 0;
-    const hipError_t e = h->p.kv_dtype == MLA_KV_BF16
-                             ? mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1, window)
-                             : mla::launch_decode_fp8_sparse(da, l.row_groups, stream, e0, e1,
-                                                             h->p.kv_dtype == MLA_KV_FP4_E2M1_E8M0, window);
+    hipError_t e = hipSuccess;
+    if (h->p.kv_dtype == MLA_KV_BF16) {
+        e = mla::launch_decode_bf16_sparse(da, l.row_groups, stream, e0, e1, window);
+    } else if (h->p.kv_dtype == MLA_KV_FP8_E4M3_E8M0) {
+        da.qx = ws + l.qx;
+        e = mla::launch_quantize_q_mx(da, stream);
+        if (e == hipSuccess) e = mla::launch_decode_fp8_mx_sparse(da, l.row_groups, stream, e0, e1, window);
+    } else {
+        e = mla::launch_decode_fp4_sparse(da, l.row_groups, stream, e0, e1, window);
+    }
     if (e != hipSuccess) return MLA_ERR_HIP;
 
     mla::CombineArgs ca{};

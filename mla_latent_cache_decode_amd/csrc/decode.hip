@@ -1,5 +1,5 @@
-// Split-KV MLA decode for an fp8 latent cache (e4m3 codes + one e8m0 scale
-// per 32) on gfx950 (CDNA4).
+// Split-KV MLA decode for an fp4 latent cache (e2m1 codes + one e8m0 scale
+// per 16) on gfx950 (CDNA4).
 //
 // What one workgroup computes ("DeepSeek R1 Architecture & Deployment Guide",
 // section 1.1): for 128 query rows (heads of one or more query positions) and
@@ -11,8 +11,9 @@
 //                    output projection downstream).
 // A split's partial result (O / l, lse) goes to the workspace for the LSE
 // combine; a sequence served by one worker is finished here directly.  The
-// row format (codes over every dimension, RoPE included, then one e8m0 scale
-// per 32 codes) is the "DeepSeek-R1" record's engine constraint (2).
+// row format (two e2m1 codes per byte over every dimension, RoPE included,
+// then one e8m0 scale per 16 values) is this build's reading of the
+// "DeepSeek-R1" record's 288-byte fp4 variant in its engine constraint (2).
 //
 // Mapping onto CDNA4 (one workgroup of 4 waves per CU):
 //  * 4 waves x 32 rows.  Each wave holds its 32 query rows as fp16 MFMA
@@ -21,8 +22,8 @@
 //    so a head's softmax statistics live in one lane pair (l, l^32) and the
 //    S^T accumulator is directly the B-operand of the PV product.
 //  * One 64-token page is one tile.  Page p + 1 streams through VGPRs while
-//    tile p is computed: 16-byte buffer loads of codes and their scale byte,
-//    dequantised in registers (v_cvt_scalef32_pk_f16_fp8) and stored into
+//    tile p is computed: buffer loads of codes and their scale bytes,
+//    dequantised in registers (v_cvt_scalef32_pk_f16_fp4) and stored into
 //    the idle fp16 LDS tile by hooks placed between the MFMA steps; one
 //    barrier per tile.  Rows past the visible tokens are never fetched (the
 //    descriptor size excludes them; the tile receives zeros).
@@ -36,16 +37,12 @@
 //  * Lazy rescaling: the running max is only raised when a tile's max
 //    exceeds it by more than 15 (log2 units), so O is rarely rescaled after
 //    the first tile and the exponentials stay <= 2^15, inside fp16 range.
-#include "decode_common.h"
+#include "decode_rowsplit.h"
 
 namespace mla {
 namespace {
 
-constexpr int kPvSteps = 4 * kMdBlocks;         // 64 MFMA steps for P.V
-constexpr float kRescaleTau = 15.0f;            // log2 units: p <= 2^15 stays inside fp16
 constexpr int kQkAhead = 2;                     // K fragment prefetch distance (k-steps)
-constexpr int kPvAhead = 2;                     // V fragment prefetch distance (steps)
-constexpr int kPMakeAt = 6;                     // P.V step (within a 16-step block) that builds the next P fragment
 
 constexpr int kLdsTiles = 2 * kTileBytes;       // 147456: two fp16 tiles
 constexpr int kQRegSteps = kDc / 16;            // 32 k-steps (q_abs) whose Q fragments live in VGPRs
@@ -57,8 +54,8 @@ constexpr int kLdsBytes = kLdsTiles + kQLdsBytes;  // 163840 = all of a CU's LDS
 // page pieces: HBM -> VGPRs -> dequantise -> fp16 LDS tile
 // ---------------------------------------------------------------------------
 //
-// A page is moved by the four waves in pieces of one 16-byte vector load
-// per lane (16 fp8 codes, plus their scale byte).  A piece is issued into registers well ahead of its use and
+// A page is moved by the four waves in pieces of one vector load per lane
+// (16 fp4 values, plus their scale byte).  A piece is issued into registers well ahead of its use and
 // stored into the tile that the next tile step reads; both halves of the
 // work are spread over the MFMA steps of the current tile, so the memory
 // path, the conversion and the matrix cores overlap.
@@ -68,105 +65,9 @@ constexpr int kLdsBytes = kLdsTiles + kQLdsBytes;  // 163840 = all of a CU's LDS
 // (the rows are never fetched) and the tile receives finite zeros.  The
 // whole offset of a lane is in the VGPR offset, so the range check sees it.
 
-// fp8 rows (D e4m3 codes, D/32 e8m0 scales, 16-byte stride).  Wave w moves
-// tokens 16w .. 16w + 15 in pieces k < 9: lane i carries token 16w + (i & 15),
-// codes 16j .. 16j + 15 with j = 4k + (i >> 4), and their scale byte j / 2.
-// The 16 dequantised halves are tile chunks 2j and 2j + 1 of that token.
-// The scale bytes come once per page: each lane loads its token's 18 bytes
-// (one 16-byte and one 4-byte load) before the page's first store, in place
-// of one byte load per piece.
-struct Fp8Pieces {
-    static constexpr int kPieces = 9;
-    // three batches of three pieces
-    static constexpr int kBatches = 3;
-    static constexpr int kStage = 3;
-    __device__ static constexpr int first(int b) { return 3 * b; }
-    static constexpr int kHookPv[3] = {0, 0, 1};
-    static constexpr int kHookAt[3] = {2, 22, 12};
-    static constexpr int kHookStride[3] = {5, 5, 10};
-    struct Stage {
-        u32x4 codes;
-    };
-    // the e8m0 scales of the lane's token: bytes 0..15 and 16..17 (+ 2 pad)
-    struct PageScales {
-        u32x4 lo;
-        uint32_t hi;
-    };
-
-    int src_lane;       // (token - tok0) * 608 + 16 * (i >> 4), inside the wave's page
-    int dst_lane;       // tile_off(token, 2 * (i >> 4)) without the column block
-    __amdgpu_buffer_rsrc_t win;   // the declared cache window (sparse gather)
-
-    // tok0: the tile token at which the wave's page descriptor starts
-    __device__ __forceinline__ Fp8Pieces(int lane, int wave, int tok0, __amdgpu_buffer_rsrc_t w) : win(w) {
-        const int t = wave * 16 + (lane & 15);
-        src_lane = (t - tok0) * kFp8RowBytes + ((lane >> 4) << 4);
-        dst_lane = tile_off(t, 2 * (lane >> 4));
-    }
-    __device__ __forceinline__ void issue(Stage& s, __amdgpu_buffer_rsrc_t r, int, int k) const {
-        s.codes = __builtin_amdgcn_raw_buffer_load_b128(r, pinned(src_lane) + k * 64, 0, 0);
-    }
-    // sparse gather: the lane's token row starts at `row` (anywhere in the
-    // cache, or a row of zeros for an entry that does not take part)
-    __device__ __forceinline__ void issue(Stage& s, const uint8_t* row, int, int k) const {
-        const int l = opaque_lane();
-        s.codes = *(const u32x4*)(row + ((l >> 4) << 4) + k * 64);
-    }
-    // sparse gather inside the declared window: the row at byte offset `row`
-    // of window descriptor `win` (an offset past the window reads zeros)
-    __device__ __forceinline__ void issue(Stage& s, uint32_t row, int, int k) const {
-        const int l = opaque_lane();
-        s.codes = __builtin_amdgcn_raw_buffer_load_b128(win, (int)(row + ((l >> 4) << 4) + k * 64), 0, 0);
-    }
-    // the scales of the lane's token sit at token * 608 + 576 (16-byte aligned)
-    __device__ __forceinline__ void load_scales(PageScales& sc, __amdgpu_buffer_rsrc_t r) const {
-        const int l = opaque_lane();
-        const int off = pinned(src_lane) - ((l >> 4) << 4) + kD;
-        sc.lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-        sc.hi = __builtin_amdgcn_raw_buffer_load_b32(r, off + 16, 0, 0);
-    }
-    __device__ __forceinline__ void load_scales(PageScales& sc, const uint8_t* row) const {
-        sc.lo = *(const u32x4*)(row + kD);
-        sc.hi = *(const uint32_t*)(row + kD + 16);
-    }
-    __device__ __forceinline__ void load_scales(PageScales& sc, uint32_t row) const {
-        sc.lo = __builtin_amdgcn_raw_buffer_load_b128(win, (int)(row + kD), 0, 0);
-        sc.hi = __builtin_amdgcn_raw_buffer_load_b32(win, (int)(row + kD + 16), 0, 0);
-    }
-    __device__ __forceinline__ void store(const Stage& s, const PageScales& sc, LDS_AS uint8_t* tile, int,
-                                          int k) const {
-        // the scale of codes 16j.. is byte j / 2 = 2k + (i >> 5) of the token's scales
-        const int h8 = (opaque_lane() >> 5) << 3;
-        const uint32_t word = k < 8 ? sc.lo[k >> 1] : sc.hi;
-        // 2^(e-127) as fp32 bits e << 23.  e = 255 (NaN) also sets the top
-        // mantissa bit, making a quiet NaN instead of infinity.  e = 0 gives
-        // 0 rather than 2^-127: every e4m3 value times 2^-127 rounds to a
-        // signed zero in fp16 anyway, so the dequantised halves are the same.
-        const uint32_t e = __builtin_amdgcn_ubfe(word, (uint32_t)((k & 1) * 16 + h8), 8);
-        const uint32_t bits = (((e + 1) >> 8) << 22) | (e << 23);
-        const float scale = __builtin_bit_cast(float, bits);
-        // chunks 2j and 2j + 1 sit in adjacent 16-byte slots (the swizzle
-        // flips at most the low slot bit between them); one at a time keeps
-        // the temporaries to four registers
-        LDS_AS uint8_t* d = tile + k * 8192;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            u32x4 h;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                h[2 * q + 0] = __builtin_bit_cast(
-                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.codes[2 * c + q], scale, false));
-                h[2 * q + 1] = __builtin_bit_cast(
-                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.codes[2 * c + q], scale, true));
-            }
-            *(LDS_AS u32x4*)(d + (dst_lane ^ (c << 4))) = h;
-        }
-    }
-};
-
 // fp4 rows (D/2 bytes of e2m1 codes, element 2i in the low nibble of byte i,
-// then one e8m0 scale per 16 values, 16-byte stride).  The same pieces as
-// the fp8 rows: lane i carries token 16w + (i & 15), the 16 values of group
+// then one e8m0 scale per 16 values, 16-byte stride).  Wave w moves tokens
+// 16w .. 16w + 15 in pieces k < 9: lane i carries token 16w + (i & 15), the 16 values of group
 // j = 4k + (i >> 4) -- 8 code bytes -- and their own scale byte j; they
 // dequantise to tile chunks 2j and 2j + 1 of that token.
 struct Fp4Pieces {
@@ -215,7 +116,9 @@ struct Fp4Pieces {
     __device__ __forceinline__ void load_scales(PageScales&, const uint8_t*) const {}
     __device__ __forceinline__ void load_scales(PageScales&, uint32_t) const {}
     __device__ __forceinline__ void store(const Stage& s, const PageScales&, LDS_AS uint8_t* tile, int, int k) const {
-        // the e8m0 scale as fp32 bits, as for the fp8 rows
+        // the e8m0 scale as fp32 bits e << 23; e = 255 (NaN) also sets the top
+        // mantissa bit, making a quiet NaN; e = 0 gives 0 rather than 2^-127,
+        // which every e2m1 value times 2^-127 rounds to in fp16 anyway
         const uint32_t e = s.scale & 0xFF;
         const float scale = __builtin_bit_cast(float, (((e + 1) >> 8) << 22) | (e << 23));
         LDS_AS uint8_t* d = tile + k * 8192;
@@ -235,18 +138,10 @@ struct Fp4Pieces {
 // ---------------------------------------------------------------------------
 // per-tile compute of one wave: 32 heads x 64 tokens
 // ---------------------------------------------------------------------------
-struct WaveState {
-    f32x16 o[kMdBlocks];     // O^T accumulator: dims x heads
-    float m;                 // running max (log2 units, lane's head)
-    float l;                 // partial sum of exp over this lane's half of the tokens
-    bool o_zero;             // nothing accumulated yet (wave-uniform)
-};
-
-// One tile step of one wave.  qk_hook(ks) runs inside Q.K^T step ks and
-// pv_hook(step) inside P.V step `step` (both compile-time); they carry the
-// page pipeline's loads and LDS stores so that these issue between MFMAs.
-// Tokens of the tile that take part: the first n_valid (dense), or the set
-// bits of `mask` (sparse: the tile's mask; bit t = token t).
+// One tile step of one wave: Q.K^T on the fp16 tile, then the shared
+// softmax and P.V.  qk_hook(ks) runs inside Q.K^T step ks and pv_hook(step)
+// inside P.V step `step` (both compile-time); they carry the page
+// pipeline's loads and LDS stores so that these issue between MFMAs.
 template <bool kSparse, typename QkHook, typename PvHook>
 __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f16x8 (&qf)[kQRegSteps],
                                              const LDS_AS uint8_t* qr, WaveState& st, int n_valid, uint64_t mask,
@@ -285,115 +180,7 @@ __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f
     });
     // the scores feed VALU work (softmax): keep them in arch VGPRs
     asm volatile("" : "+v"(s0), "+v"(s1));
-
-    // ---- softmax.  Tokens >= n_valid (tail of the sequence / causal limit)
-    // are masked: excluded from the max and given p = 0.  The token of
-    // register r is c_r + 4*hi (+32 for s1); compare c_r with nv_lane.
-    const int nv_lane = n_valid - (hi << 2);
-    const uint64_t m_lane = mask >> (hi << 2);
-    // does token c + 4 hi of the tile take part (c compile-time)
-    auto vis = [&](int c) -> bool {
-        if constexpr (kSparse) return (m_lane >> c) & 1;
-        else return c < nv_lane;
-    };
-    float mx = -__builtin_inff();
-    if (kSparse ? mask == ~0ull : n_valid >= kPage) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int c_r = ((r >> 2) << 3) + (r & 3);
-            mx = fmaxf(mx, vis(c_r) ? s0[r] : -__builtin_inff());
-            mx = fmaxf(mx, vis(c_r + 32) ? s1[r] : -__builtin_inff());
-        }
-    }
-    mx = pair_max(mx);
-    const float mx2 = mx * scale_log2;
-    const bool need = mx2 > st.m + kRescaleTau;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? mx2 : st.m;
-        if (!st.o_zero) {
-            const float alpha = need ? fast_exp2(st.m - m_new) : 1.0f;
-#pragma unroll
-            for (int md = 0; md < kMdBlocks; ++md) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) st.o[md][r] = scale_acc(st.o[md][r], alpha);
-            }
-            st.l *= alpha;
-        }
-        st.m = m_new;
-    }
-    // P fragment kb (tokens of S^T registers 8(kb&1) .. +7 of s0 / s1) in
-    // fp16; fragment 0 now, the others inside the P.V loop, where their
-    // exponentials issue between MFMAs
-    const float neg_m = -st.m;
-    float lsum = 0.f;
-    auto make_p = [&](auto kb_c) -> f16x8 {
-        constexpr int kb = decltype(kb_c)::value;
-        const f32x16& sv = kb < 2 ? s0 : s1;
-        f16x8 f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int r = (kb & 1) * 8 + e;
-            const int c_r = ((r >> 2) << 3) + (r & 3) + (kb >= 2 ? 32 : 0);
-            const float x = vis(c_r) ? fast_exp2(fmaf(sv[r], scale_log2, neg_m)) : 0.f;
-            lsum += x;
-            f[e] = (_Float16)x;
-        }
-        return f;
-    };
-    f16x8 pf[4];
-    pf[0] = make_p(std::integral_constant<int, 0>{});
-
-    // ---- O^T += V^T P^T.  Step s covers (kb = s >> 4, md = s & 15); its V^T
-    // fragment is two transposed reads (tokens kb*16 + e4*8 + tok_lane, dims
-    // md*32 + dim_lane), issued kPvAhead steps ahead into rotating buffers.
-    __builtin_amdgcn_sched_barrier(0);
-    // vp[m][e]: tokens 8e + tok (the swizzle sees bit 3 of the token, which
-    // flips the low slot bit: address ^ 16), dims m*32 + dim; the step's
-    // column block and 16-token block are added as immediate offsets
-    const LDS_AS uint8_t* vp[2][2];
-    {
-        const int g = lane >> 4, li = lane & 15;
-        const int tok = ((g >> 1) << 2) + (li >> 2);
-        const int dim = ((g & 1) << 4) + ((li & 3) << 2);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int o = tile_off(tok, (m * 32 + dim) >> 3) + (dim & 7) * 2;
-            vp[m][0] = tile + o;
-            vp[m][1] = tile + (o ^ 16) + 8 * 128;
-        }
-    }
-    constexpr int kVBufs = kPvAhead + 2;
-    f16x8 vf[kVBufs];
-    auto read_v = [&](auto step_c) -> f16x8 {
-        constexpr int step = decltype(step_c)::value;
-        constexpr int kb_ = step >> 4, md = step & 15;
-        constexpr int off = (md >> 1) * 8192 + kb_ * 16 * 128;
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][0] + off));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][1] + off));
-        return __builtin_bit_cast(f16x8, i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-    };
-    static_for<0, kPvAhead>([&](auto i) { vf[decltype(i)::value] = read_v(i); });
-    static_for<0, kPvSteps>([&](auto step_c) {
-        constexpr int step = decltype(step_c)::value;
-        if constexpr (step + kPvAhead < kPvSteps)
-            vf[(step + kPvAhead) % kVBufs] = read_v(std::integral_constant<int, step + kPvAhead>{});
-        st.o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[step % kVBufs], pf[step >> 4], st.o[step & 15],
-                                                                  0, 0, 0);
-        // VALU and memory work issues while the MFMA runs
-        if constexpr ((step & 15) == kPMakeAt && (step >> 4) < 3)
-            pf[(step >> 4) + 1] = make_p(std::integral_constant<int, (step >> 4) + 1>{});
-        pv_hook(step_c);
-        __builtin_amdgcn_sched_barrier(0);
-    });
-    // keep the accumulator's home in AGPRs (it is only touched by MFMA in the
-    // steady state); VALU users copy out and back
-#pragma unroll
-    for (int md = 0; md < kMdBlocks; ++md) asm volatile("" : "+a"(st.o[md]));
-    st.l += lsum;
-    st.o_zero = false;
+    softmax_pv<kSparse>(tile, st, s0, s1, n_valid, mask, scale_log2, lane, pv_hook);
 }
 
 // ---------------------------------------------------------------------------
@@ -414,12 +201,12 @@ __device__ __attribute__((aligned(256))) uint8_t g_sparse_zero_row[kSparseZeroRo
 // kWin (sparse only): the caller has declared that the whole cache lies in
 // the first kGatherWindow bytes from its base; rows are then gathered with
 // 32-bit buffer offsets.
-template <int PS, bool kSparse, bool kFp4, bool kWin = false>
+template <int PS, bool kSparse, bool kWin = false>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArgs a) {
-    typedef std::conditional_t<kFp4, Fp4Pieces, Fp8Pieces> Pieces;
+    typedef Fp4Pieces Pieces;
     typedef PageGeom<PS> Geom;
     constexpr int kPieces = Pieces::kPieces;
-    constexpr int kRowBytes = kFp4 ? kFp4RowBytes : kFp8RowBytes;
+    constexpr int kRowBytes = kFp4RowBytes;
     static_assert(Geom::kRangeTok % 16 == 0, "a wave's 16 tokens lie in one page");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
@@ -765,36 +552,26 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
     }
 }
 
-template <bool kFp4>
-hipError_t launch_decode_quantised(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                                   hipEvent_t ev_stop) {
+}  // namespace
+
+hipError_t launch_decode_fp4(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                             hipEvent_t ev_stop) {
     const dim3 grid(a.num_workers * row_groups);
     switch (a.page_size) {
-        case 16: return launch_with_events(mla_decode_kernel<16, false, kFp4>, grid, stream, ev_start, ev_stop, a);
-        case 32: return launch_with_events(mla_decode_kernel<32, false, kFp4>, grid, stream, ev_start, ev_stop, a);
-        case 64: return launch_with_events(mla_decode_kernel<64, false, kFp4>, grid, stream, ev_start, ev_stop, a);
-        case 128: return launch_with_events(mla_decode_kernel<128, false, kFp4>, grid, stream, ev_start, ev_stop, a);
-        case 256: return launch_with_events(mla_decode_kernel<256, false, kFp4>, grid, stream, ev_start, ev_stop, a);
+        case 16: return launch_with_events(mla_decode_kernel<16, false>, grid, stream, ev_start, ev_stop, a);
+        case 32: return launch_with_events(mla_decode_kernel<32, false>, grid, stream, ev_start, ev_stop, a);
+        case 64: return launch_with_events(mla_decode_kernel<64, false>, grid, stream, ev_start, ev_stop, a);
+        case 128: return launch_with_events(mla_decode_kernel<128, false>, grid, stream, ev_start, ev_stop, a);
+        case 256: return launch_with_events(mla_decode_kernel<256, false>, grid, stream, ev_start, ev_stop, a);
         default: return hipErrorInvalidValue;
     }
 }
 
-}  // namespace
-
-hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                             hipEvent_t ev_stop, bool fp4) {
-    return fp4 ? launch_decode_quantised<true>(a, row_groups, stream, ev_start, ev_stop)
-               : launch_decode_quantised<false>(a, row_groups, stream, ev_start, ev_stop);
-}
-
-hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                                    hipEvent_t ev_stop, bool fp4, bool window) {
+hipError_t launch_decode_fp4_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                                    hipEvent_t ev_stop, bool window) {
     const dim3 grid(a.num_workers * row_groups);
-    if (window)
-        return fp4 ? launch_with_events(mla_decode_kernel<64, true, true, true>, grid, stream, ev_start, ev_stop, a)
-                   : launch_with_events(mla_decode_kernel<64, true, false, true>, grid, stream, ev_start, ev_stop, a);
-    return fp4 ? launch_with_events(mla_decode_kernel<64, true, true>, grid, stream, ev_start, ev_stop, a)
-               : launch_with_events(mla_decode_kernel<64, true, false>, grid, stream, ev_start, ev_stop, a);
+    return window ? launch_with_events(mla_decode_kernel<64, true, true>, grid, stream, ev_start, ev_stop, a)
+                  : launch_with_events(mla_decode_kernel<64, true>, grid, stream, ev_start, ev_stop, a);
 }
 
 }  // namespace mla

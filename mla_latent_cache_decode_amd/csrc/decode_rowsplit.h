@@ -1,0 +1,152 @@
+// Row-split softmax and P.V shared by the quantised-cache decode kernels
+// ("DeepSeek R1 Architecture & Deployment Guide", section 1.1: softmax of the
+// scores over the context, then the softmax-weighted sum of the latent rows).
+// Each wave owns 32 query rows and their O^T accumulator (512 dims x 32 rows,
+// 256 AGPRs); its S^T scores (two 32-token blocks) are the B operand of P.V
+// after the softmax, so no weights are exchanged between waves.
+#pragma once
+
+#include "decode_common.h"
+
+namespace mla {
+namespace {
+
+constexpr int kPvSteps = 4 * kMdBlocks;         // 64 MFMA steps for P.V
+constexpr float kRescaleTau = 15.0f;            // log2 units: p <= 2^15 stays inside fp16
+constexpr int kPvAhead = 2;                     // V fragment prefetch distance (steps)
+constexpr int kPMakeAt = 6;                     // P.V step (within a 16-step block) that builds the next P fragment
+
+// per-wave state of the online softmax and the O accumulator
+struct WaveState {
+    f32x16 o[kMdBlocks];     // O^T accumulator: dims x heads
+    float m;                 // running max (log2 units, lane's head)
+    float l;                 // partial sum of exp over this lane's half of the tokens
+    bool o_zero;             // nothing accumulated yet (wave-uniform)
+};
+
+// Softmax of the tile's scores s0 (tokens 0..31) and s1 (tokens 32..63) in
+// S^T MFMA layout, then O^T += V^T P^T with V^T read from the fp16 tile
+// `vtile` (token t's 16-byte chunk c at tile_off(t, c)).  pv_hook(step) runs
+// inside P.V step `step` (compile-time).  Tokens of the tile that take part:
+// the first n_valid (dense), or the set bits of `mask` (sparse: bit t =
+// token t).  Lazy rescaling: the running max is raised only when the tile's
+// max exceeds it by more than kRescaleTau, and O is then rescaled in place.
+// `lane` is the caller's opaque_lane().
+template <bool kSparse, typename PvHook>
+__device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveState& st, f32x16& s0, f32x16& s1,
+                                           int n_valid, uint64_t mask, float scale_log2, int lane, PvHook&& pv_hook) {
+    const int hi = lane >> 5;
+    const LDS_AS uint8_t* tile = vtile;
+
+    // ---- softmax.  Tokens >= n_valid (tail of the sequence / causal limit)
+    // are masked: excluded from the max and given p = 0.  The token of
+    // register r is c_r + 4*hi (+32 for s1); compare c_r with nv_lane.
+    const int nv_lane = n_valid - (hi << 2);
+    const uint64_t m_lane = mask >> (hi << 2);
+    // does token c + 4 hi of the tile take part (c compile-time)
+    auto vis = [&](int c) -> bool {
+        if constexpr (kSparse) return (m_lane >> c) & 1;
+        else return c < nv_lane;
+    };
+    float mx = -__builtin_inff();
+    if (kSparse ? mask == ~0ull : n_valid >= kPage) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int c_r = ((r >> 2) << 3) + (r & 3);
+            mx = fmaxf(mx, vis(c_r) ? s0[r] : -__builtin_inff());
+            mx = fmaxf(mx, vis(c_r + 32) ? s1[r] : -__builtin_inff());
+        }
+    }
+    mx = pair_max(mx);
+    const float mx2 = mx * scale_log2;
+    const bool need = mx2 > st.m + kRescaleTau;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mx2 : st.m;
+        if (!st.o_zero) {
+            const float alpha = need ? fast_exp2(st.m - m_new) : 1.0f;
+#pragma unroll
+            for (int md = 0; md < kMdBlocks; ++md) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st.o[md][r] = scale_acc(st.o[md][r], alpha);
+            }
+            st.l *= alpha;
+        }
+        st.m = m_new;
+    }
+    // P fragment kb (tokens of S^T registers 8(kb&1) .. +7 of s0 / s1) in
+    // fp16; fragment 0 now, the others inside the P.V loop, where their
+    // exponentials issue between MFMAs
+    const float neg_m = -st.m;
+    float lsum = 0.f;
+    auto make_p = [&](auto kb_c) -> f16x8 {
+        constexpr int kb = decltype(kb_c)::value;
+        const f32x16& sv = kb < 2 ? s0 : s1;
+        f16x8 f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int r = (kb & 1) * 8 + e;
+            const int c_r = ((r >> 2) << 3) + (r & 3) + (kb >= 2 ? 32 : 0);
+            const float x = vis(c_r) ? fast_exp2(fmaf(sv[r], scale_log2, neg_m)) : 0.f;
+            lsum += x;
+            f[e] = (_Float16)x;
+        }
+        return f;
+    };
+    f16x8 pf[4];
+    pf[0] = make_p(std::integral_constant<int, 0>{});
+
+    // ---- O^T += V^T P^T.  Step s covers (kb = s >> 4, md = s & 15); its V^T
+    // fragment is two transposed reads (tokens kb*16 + e4*8 + tok_lane, dims
+    // md*32 + dim_lane), issued kPvAhead steps ahead into rotating buffers.
+    __builtin_amdgcn_sched_barrier(0);
+    // vp[m][e]: tokens 8e + tok (the swizzle sees bit 3 of the token, which
+    // flips the low slot bit: address ^ 16), dims m*32 + dim; the step's
+    // column block and 16-token block are added as immediate offsets
+    const LDS_AS uint8_t* vp[2][2];
+    {
+        const int g = lane >> 4, li = lane & 15;
+        const int tok = ((g >> 1) << 2) + (li >> 2);
+        const int dim = ((g & 1) << 4) + ((li & 3) << 2);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int o = tile_off(tok, (m * 32 + dim) >> 3) + (dim & 7) * 2;
+            vp[m][0] = tile + o;
+            vp[m][1] = tile + (o ^ 16) + 8 * 128;
+        }
+    }
+    constexpr int kVBufs = kPvAhead + 2;
+    f16x8 vf[kVBufs];
+    auto read_v = [&](auto step_c) -> f16x8 {
+        constexpr int step = decltype(step_c)::value;
+        constexpr int kb_ = step >> 4, md = step & 15;
+        constexpr int off = (md >> 1) * 8192 + kb_ * 16 * 128;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][0] + off));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][1] + off));
+        return __builtin_bit_cast(f16x8, i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+    };
+    static_for<0, kPvAhead>([&](auto i) { vf[decltype(i)::value] = read_v(i); });
+    static_for<0, kPvSteps>([&](auto step_c) {
+        constexpr int step = decltype(step_c)::value;
+        if constexpr (step + kPvAhead < kPvSteps)
+            vf[(step + kPvAhead) % kVBufs] = read_v(std::integral_constant<int, step + kPvAhead>{});
+        st.o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[step % kVBufs], pf[step >> 4], st.o[step & 15],
+                                                                  0, 0, 0);
+        // VALU and memory work issues while the MFMA runs
+        if constexpr ((step & 15) == kPMakeAt && (step >> 4) < 3)
+            pf[(step >> 4) + 1] = make_p(std::integral_constant<int, (step >> 4) + 1>{});
+        pv_hook(step_c);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    // keep the accumulator's home in AGPRs (it is only touched by MFMA in the
+    // steady state); VALU users copy out and back
+#pragma unroll
+    for (int md = 0; md < kMdBlocks; ++md) asm volatile("" : "+a"(st.o[md]));
+    st.l += lsum;
+    st.o_zero = false;
+}
+
+}  // namespace
+}  // namespace mla

@@ -24,6 +24,8 @@ constexpr int kFp8RowBytes = (kFp8Payload + 15) / 16 * 16;  // 608
 // D/2 bytes of e2m1 codes, two per byte, then one e8m0 scale per 16 values
 constexpr int kFp4Payload = kD / 2 + kD / 16;                // 324
 constexpr int kFp4RowBytes = (kFp4Payload + 15) / 16 * 16;  // 336
+// the fp8 decode's query rows: two terms (q_hi, q_lo), each in the fp8 row format
+constexpr int kMxQxRowBytes = 2 * kFp8RowBytes;             // 1216
 constexpr int kRowsPerGroup = 128;            // query rows one workgroup serves
 constexpr int kRowsPerWave = 32;
 constexpr int kDecodeThreads = 256;           // 4 waves of 64
@@ -50,6 +52,7 @@ struct DecodeArgs {
     float* out;                 // [B][M][kDc]
     float* lse;                 // [B][M] or null
     PlanView plan;
+    uint8_t* qx;                // fp8 cache: the two-term query rows [B][M][kMxQxRowBytes] (workspace)
     int64_t page_bytes;         // bytes per page
     int32_t page_size;          // tokens per page block (16 .. 256, a power of two)
     int32_t batch;
@@ -99,21 +102,28 @@ struct CombineArgs {
 // stream packets).
 hipError_t launch_decode_bf16(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                               hipEvent_t ev_stop);
-// the fp8-family kernel serves both quantised formats (fp4: the e2m1 row)
-hipError_t launch_decode_fp8(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                             hipEvent_t ev_stop, bool fp4 = false);
+// the fp4 cache (e2m1 codes, e8m0 per 16): dequantised into an fp16 tile
+hipError_t launch_decode_fp4(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                             hipEvent_t ev_stop);
+// the fp8 cache's dense decode: quantise the queries into a.qx (two e4m3
+// terms with e8m0 scales per 32), then the block-scaled decode
+hipError_t launch_quantize_q_mx(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_fp8_mx(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                                hipEvent_t ev_stop);
+hipError_t launch_decode_fp8_mx_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                                       hipEvent_t ev_stop, bool window);
 // window: the cache lies in the first kGatherWindow bytes (MLA_FLAG_KV_WITHIN_4GIB)
 hipError_t launch_decode_bf16_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                                      hipEvent_t ev_stop, bool window);
-hipError_t launch_decode_fp8_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
-                                    hipEvent_t ev_stop, bool fp4, bool window);
+hipError_t launch_decode_fp4_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                                    hipEvent_t ev_stop, bool window);
 // max_splits: an upper bound on the splits of one sequence (the worker
 // count); it sizes the combine's LDS and picks its shape.
 hipError_t launch_combine(const CombineArgs& a, int max_splits, hipStream_t stream);
 
 // Bytes of the per-device scratch that mla_decode_run_noalloc uses as its
 // workspace (MLA_NOALLOC_SCRATCH_BYTES in the public header).
-constexpr size_t kNoAllocScratchBytes = (size_t)72 << 20;
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
 // The device address of `device`'s copy of that scratch; `device` must be
 // current.  Taken with hipGetSymbolAddress on the first call per device and
 // kept; later calls return the kept address.  Thread-safe.

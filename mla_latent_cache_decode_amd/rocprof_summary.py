@@ -40,13 +40,18 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # the source files each decode kernel is built from
 KERNEL_SOURCES = {
     "mla_decode_bf16_kernel": ("csrc/decode_bf16.hip", "csrc/decode_common.h", "csrc/mla_internal.h"),
-    "mla_decode_kernel": ("csrc/decode.hip", "csrc/decode_common.h", "csrc/mla_internal.h"),
+    "mla_decode_kernel": ("csrc/decode.hip", "csrc/decode_rowsplit.h", "csrc/decode_common.h", "csrc/mla_internal.h"),
+    "mla_decode_mx_kernel": ("csrc/decode_mx.hip", "csrc/decode_rowsplit.h", "csrc/decode_common.h",
+                             "csrc/mla_internal.h"),
 }
 
 
-def kernel_for_dtype(kv_dtype: str) -> str:
-    """Name of the decode kernel that serves a cache dtype."""
-    return "mla_decode_bf16_kernel" if kv_dtype == "bf16" else "mla_decode_kernel"
+def kernel_for_dtype(kv_dtype: str, sparse: bool = False) -> str:
+    """Name of the decode kernel that serves a cache dtype (the dense and the
+    sparse decode of one dtype share their kernel)."""
+    if kv_dtype == "bf16":
+        return "mla_decode_bf16_kernel"
+    return "mla_decode_mx_kernel" if kv_dtype == "fp8" else "mla_decode_kernel"
 
 
 def _code_only(text: str) -> str:

@@ -71,6 +71,10 @@ def test_noalloc_default_plan_fits_the_scratch():
         dec = mla.MlaDecode(max_batch=1024, s_q=s_q, n_h=n_h, max_blocks_per_seq=64,
                             softmax_scale=0.072)
         assert dec.workspace_size(1024) <= mla.NOALLOC_SCRATCH_BYTES, (s_q, n_h)
+    # the fp8 cache adds its two-term query rows (1216 bytes each): 400
+    # sequences of 128 heads still fit
+    dec = mla.MlaDecode(max_batch=400, n_h=128, max_blocks_per_seq=64, kv_dtype="fp8", softmax_scale=0.072)
+    assert dec.workspace_size(400) <= mla.NOALLOC_SCRATCH_BYTES
 
 
 def test_noalloc_rejects_a_plan_beyond_the_scratch():
