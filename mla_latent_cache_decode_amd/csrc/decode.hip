@@ -67,7 +67,8 @@ constexpr int kLdsBytes = kLdsTiles + kQLdsBytes;  // 163840 = all of a CU's LDS
 
 // fp4 rows (D/2 bytes of e2m1 codes, element 2i in the low nibble of byte i,
 // then one e8m0 scale per 16 values, 16-byte stride).  Wave w moves tokens
-// 16w .. 16w + 15 in pieces k < 9: lane i carries token 16w + (i & 15), the 16 values of group
+// 16w .. 16w + 15 in pieces k < 9: lane i carries one of them (see the
+// constructor), the 16 values of group
 // j = 4k + (i >> 4) -- 8 code bytes -- and their own scale byte j; they
 // dequantise to tile chunks 2j and 2j + 1 of that token.
 struct Fp4Pieces {
@@ -89,8 +90,11 @@ struct Fp4Pieces {
     int dst_lane;       // tile_off(token, 2 * (i >> 4)) without the column block
     __amdgpu_buffer_rsrc_t win;   // the declared cache window (sparse gather)
 
-    __device__ __forceinline__ Fp4Pieces(int lane, int wave, int tok0, __amdgpu_buffer_rsrc_t w) : win(w) {
-        const int t = wave * 16 + (lane & 15);
+    // spread: lane i carries token 16w + store_token(i & 15) (conflict-free
+    // tile stores); the sparse gather keeps token 16w + (i & 15), whose row
+    // address the lane swaps deliver
+    __device__ __forceinline__ Fp4Pieces(int lane, int wave, int tok0, __amdgpu_buffer_rsrc_t w, bool spread) : win(w) {
+        const int t = wave * 16 + (spread ? store_token(lane & 15) : (lane & 15));
         src_lane = (t - tok0) * kFp4RowBytes + ((lane >> 4) << 3);
         dst_lane = tile_off(t, 2 * (lane >> 4));
     }
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
                 *(LDS_AS f16x8*)(qr_lds + (ks - kQRegSteps) * 1024) = qf[ks];
         };
         const f16x8(&qreg)[kQRegSteps] = *reinterpret_cast<const f16x8(*)[kQRegSteps]>(&qf[0]);
-        const Pieces pc(opaque_lane(), wave, tok0, make_rsrc(a.kv, kWin ? (int)kGatherWindow : 0));
+        const Pieces pc(opaque_lane(), wave, tok0, make_rsrc(a.kv, kWin ? (int)kGatherWindow : 0), !kSparse);
 
         // ---- Page pipeline, one barrier per tile.  Pieces stream through
         // VGPRs (converted or dequantised in registers) into the idle
@@ -520,35 +524,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         // the last tile issued loads of pages past p_hi: zero-size
         // descriptors, nothing is fetched, and they are never waited for
 
-        // epilogue: normalise and write final output or the split's partial
-        if (active) {
-            const int lane = tid & 63;
-            const float l_tot = pair_sum(st.l);
-            const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-            const float lse_v = l_tot > 0.f ? (st.m + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
-                                            : -__builtin_inff();
-            const int row = row0 + (lane & 31);
-            const int hi = lane >> 5;
-            float* dst = a.out + ((int64_t)b * M + row) * kDc + hi * 4;
-            uint16_t* pdst = a.plan.part_o + ((int64_t)(slot < 0 ? 0 : slot) * M + row) * kDc + hi * 4;
-#pragma unroll
-            for (int md = 0; md < kMdBlocks; ++md) {
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    f32x4 v = {st.o[md][r4 * 4 + 0] * inv, st.o[md][r4 * 4 + 1] * inv,
-                               st.o[md][r4 * 4 + 2] * inv, st.o[md][r4 * 4 + 3] * inv};
-                    if (slot < 0) *(f32x4*)(dst + md * 32 + r4 * 8) = v;
-                    else store_partial4(pdst + md * 32 + r4 * 8, v);
-                }
-            }
-            if (lane < 32) {
-                if (slot < 0) {
-                    if (a.lse) a.lse[(int64_t)b * M + row] = lse_v;
-                } else {
-                    a.plan.part_lse[(int64_t)row * a.plan.slots + slot] = lse_v;
-                }
-            }
-        }
+        rowsplit_epilogue(a, st, lds + wave * (kRowsPerWave * 1024), b, M, row0, slot, active);
+        // the next segment's first page and q_R fragments land in these bytes
+        __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
+        wg_barrier();
     }
 }
 

@@ -59,6 +59,16 @@ __device__ __forceinline__ T ld_const(const T* p) {
 // adjacent chunks; slot bit 2 = t1 separates T from T+2 (and T+1 from T+3).
 __device__ __forceinline__ int sw(int t) { return (((t >> 1) & 1) << 2) | (((t >> 2) & 1) << 1) | ((t >> 3) & 1); }
 
+// The token (of 16) whose row lane i of a 16-lane group converts and stores.
+// 16-byte LDS stores are served 8 lanes (128 bytes) per pass, unlike 16-byte
+// reads (16 lanes, 256 bytes): tokens t and t + 1 differ only in address
+// bit 7, so they share banks within a 128-byte pass.  Even tokens in lanes
+// 0 .. 7 and odd ones in lanes 8 .. 15 give each pass 8 tokens with distinct
+// sw(t), i.e. 8 distinct 16-byte bank groups (SQ_LDS_BANK_CONFLICT per
+// decode: fp4_b64 5.7M -> 0 cycles, fp8_b64 6.0M -> 1.5M; the reads, 16
+// lanes a pass, stay conflict-free either way).
+__device__ __forceinline__ int store_token(int i) { return ((i & 7) << 1) | ((i >> 3) & 1); }
+
 // byte offset of (token t, chunk c) inside a tile (16-bit elements)
 __device__ __forceinline__ int tile_off(int t, int c) {
     return (((c >> 3) << 9) + (t << 3) + ((c & 7) ^ sw(t))) << 4;

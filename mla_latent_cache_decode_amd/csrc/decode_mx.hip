@@ -467,10 +467,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
                 const uint32_t shi = *(const LDS_AS uint32_t*)(raw + tile_off(t, kMxScaleChunk + 1));
                 ks[blk] = mx_scales(slo, shi, h);
             }
-            // V dequantisation: lane i of wave w converts token 16w + (i & 15),
-            // chunks c = 4k + (i >> 4) (codes 16c .. 16c + 15, scale byte c / 2)
+            // V dequantisation: lane i of wave w converts token 16w +
+            // store_token(i & 15), chunks c = 4k + (i >> 4) (codes 16c .. 16c + 15, scale byte c / 2)
             // into fp16 chunks 2c, 2c + 1 of the V tile
-            const int v_tok = 16 * wave + (lane & 15);
+            const int v_tok = 16 * wave + store_token(lane & 15);
             const u32x4 v_sc = *(const LDS_AS u32x4*)(raw + tile_off(v_tok, kMxScaleChunk));
             const int v_src = tile_off(v_tok, lane >> 4);           // chunk 4k + (i >> 4) adds k * 4 chunks
             const int v_dst = tile_off(v_tok, 2 * (lane >> 4));
@@ -559,35 +559,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
         // the last tile fetched page p_hi through a zero-size descriptor:
         // nothing was read and its zeros are never used
 
-        // epilogue: normalise and write final output or the split's partial
-        if (active) {
-            const int lane = tid & 63;
-            const float l_tot = pair_sum(st.l);
-            const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-            const float lse_v = l_tot > 0.f ? (st.m + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
-                                            : -__builtin_inff();
-            const int row = row0 + (lane & 31);
-            const int hi = lane >> 5;
-            float* dst = a.out + ((int64_t)b * M + row) * kDc + hi * 4;
-            uint16_t* pdst = a.plan.part_o + ((int64_t)(slot < 0 ? 0 : slot) * M + row) * kDc + hi * 4;
-#pragma unroll
-            for (int md = 0; md < kMdBlocks; ++md) {
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    f32x4 v = {st.o[md][r4 * 4 + 0] * inv, st.o[md][r4 * 4 + 1] * inv,
-                               st.o[md][r4 * 4 + 2] * inv, st.o[md][r4 * 4 + 3] * inv};
-                    if (slot < 0) *(f32x4*)(dst + md * 32 + r4 * 8) = v;
-                    else store_partial4(pdst + md * 32 + r4 * 8, v);
-                }
-            }
-            if (lane < 32) {
-                if (slot < 0) {
-                    if (a.lse) a.lse[(int64_t)b * M + row] = lse_v;
-                } else {
-                    a.plan.part_lse[(int64_t)row * a.plan.slots + slot] = lse_v;
-                }
-            }
-        }
+        rowsplit_epilogue(a, st, lds + wave * (kRowsPerWave * 1024), b, M, row0, slot, active);
+        // the next segment's first page lands in these bytes
+        __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
+        wg_barrier();
     }
 }
 
