@@ -175,6 +175,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
         auto load_phys = [&](int p) -> int {
             return __builtin_amdgcn_raw_buffer_load_b32(bt, Geom::entry(p, tok0) * 4, 0, 0);
         };
+        // the same by a scalar load, for the segment prologue: its wait
+        // (lgkmcnt) does not queue behind the direct-to-LDS query loads
+        const int n_entries = PS < kPage ? min(Geom::entries(p_hi), a.max_blocks) : Geom::entries(p_hi);
+        auto load_phys_s = [&](int p) -> int {
+            const int e = __builtin_amdgcn_readfirstlane(Geom::entry(p, tok0));
+            const bool in = e < n_entries;
+            const int v = ld_const(a.block_table + (int64_t)b * a.max_blocks + (in ? e : 0));
+            return in ? v : 0;
+        };
         // rows of tile p this wave's page holds for the workgroup (0 past p_hi); uniform
         auto page_rows = [&](int p) {
             return __builtin_amdgcn_readfirstlane(
@@ -281,9 +290,47 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
         rs.m = -__builtin_inff();
         // a second pass runs only if a block overflowed the first pass's m
         for (int pass = 0;; ++pass) {
-        // segment prologue: the first block-table entries, the queries while
-        // they are in flight (loads complete in order, so waiting for the
-        // entry does not wait for the queries), then the first page
+        // segment prologue: the first half of the queries, the first
+        // block-table entries (or index-list entries), the first page, the
+        // second half of the queries.  The queries go first: the compiler's
+        // waits for the entries count only its own loads, so a wait for an
+        // entry also waits for every direct-to-LDS load issued before it.
+        // this wave's 32 query rows as bf16 B-operands: lane i holds row
+        // i & 31, elements 8 (i >> 5) .. + 7 of each 16-element k-step.
+        // Loaded per pass (from L2 on a second pass) so that they are not
+        // live across the epilogue.  The rows (36 KiB, contiguous) come in
+        // two halves of 18 k-steps through this wave's quarter of tiles[1],
+        // which is free until the loop loads page p_lo + 1: direct-to-LDS
+        // loads of whole 1 KiB runs, then fragment reads.  A load of lanes
+        // reading 32 rows each would touch 32 lines per instruction; these
+        // touch 9 to 11.  16-byte chunk m = 36 r + k of a half (row r, byte
+        // 16 k of the row's half) sits at LDS chunk m ^ ((m >> 4) & 3), so
+        // each load still covers one contiguous KiB (in permuted order) and
+        // the 16 rows one fragment read serves per pass hit 16 distinct bank
+        // groups.
+        bf16x8 qf[kKSteps];
+        LDS_AS uint8_t* const qst = tiles[1] + wave * (kTileBytes / 4);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t*)(a.q + ((int64_t)b * M + (active ? row0 : 0)) * kD),
+                                                    kRowsPerWave * kD * 2);
+        auto q_half_load = [&](int h) {
+            const int l = opaque_lane();
+            const int pl = l ^ ((l >> 4) & 3);
+#pragma unroll
+            for (int c = 0; c < kKSteps / 2; ++c) {
+                const int m = 64 * c + pl, r = m / 36, k = m - 36 * r;
+                dma16_shared(rq, r * (kD * 2) + h * kD + 16 * k, (uint32_t)(uintptr_t)(qst + c * 1024));
+            }
+        };
+        auto q_half_read = [&](int h) {
+            const int l = opaque_lane();
+            const int m0 = (l & 31) * 36 + (l >> 5);
+#pragma unroll
+            for (int j = 0; j < kKSteps / 2; ++j) {
+                const int m = m0 + 2 * j;
+                qf[h * (kKSteps / 2) + j] = *(const LDS_AS bf16x8*)(qst + ((m ^ ((m >> 4) & 3)) << 4));
+            }
+        };
+        q_half_load(0);
         int phys0 = 0, phys_next = 0, rows0 = 0;
         uint32_t mk_lo = ~0u, mk_hi = ~0u;       // sparse: mask of the current tile
         uint32_t mk_next_lo = ~0u, mk_next_hi = ~0u;
@@ -295,23 +342,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
             pend0 = expand(iv0, p_lo, mk_lo, mk_hi);
             pend = expand(iv1, p_lo + 1, mk_next_lo, mk_next_hi);
         } else {
-            phys0 = load_phys(p_lo);
-            phys_next = load_phys(p_lo + 1);
-            rows0 = page_rows(p_lo);
-            // held in an SGPR from here: a VGPR copy would be spilled across the
-            // query loads, and its reload would wait for all of them
+            phys0 = load_phys_s(p_lo);
+            phys_next = load_phys_s(p_lo + 1);
+            // computed here from an opaque copy of n_load, and held in an SGPR:
+            // a copy hoisted out of the pass loop would be spilled, and its
+            // reload would wait for every load in flight
+            int nl = n_load;
+            asm volatile("" : "+s"(nl));
+            rows0 = __builtin_amdgcn_readfirstlane(
+                p_lo < p_hi ? min(max(nl - p_lo * kPage - tok0, 0), Geom::kRangeTok) : 0);
             asm volatile("" : "+s"(rows0));
-        }
-        // this wave's 32 query rows as bf16 B-operands: lane i holds row
-        // i & 31, elements 8 (i >> 5) .. + 7 of each 16-element k-step.
-        // Loaded per pass (from L2 on a second pass) so that they are not
-        // live across the epilogue.
-        bf16x8 qf[kKSteps];
-        {
-            const int row = active ? row0 + (lane0 & 31) : 0;
-            const uint16_t* qrow = a.q + ((int64_t)b * M + row) * kD + (lane0 >> 5) * 8;
-#pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8*)(qrow + ks * 16);
         }
         if constexpr (kSparse) {
             const u32x2 rw0 = rows_of(pend0);
@@ -321,6 +361,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
 #pragma unroll
             for (int k = 0; k < kDmaPerWave; ++k) dma_piece(r0, tiles[0], k);
         }
+        // the first half landed (only the page's loads may still be in
+        // flight); its reads complete before the second half overwrites it
+        __builtin_amdgcn_s_waitcnt(VMCNT_IMM(kDmaPerWave));
+        q_half_read(0);
+        __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
+        q_half_load(1);
         rs.l = 0.f;
         bool overflow = false;
         f32x16 o[4][4];                   // O^T blocks [dim block][row block]
@@ -329,6 +375,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_bf16_kernel(Deco
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb) o[db][hb] = f32x16{};
         __builtin_amdgcn_s_waitcnt(VMCNT0_IMM);
+        q_half_read(1);
+        // every wave's reads of tiles[1] complete before any wave loads
+        // page p_lo + 1 into it
+        __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
         wg_barrier();
 
         for (int p = p_lo; p < p_hi; ++p) {

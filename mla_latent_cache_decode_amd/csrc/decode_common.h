@@ -33,6 +33,8 @@ static_assert(kChunks % 8 == 0, "row must be whole 64-dim column blocks");
 
 #define LGKMCNT0_IMM 0xC07F
 #define VMCNT0_IMM 0x0F70
+// wait until at most n (< 64) vector-memory operations are outstanding
+#define VMCNT_IMM(n) (0x0F70 | ((n) & 15) | ((((n) >> 4) & 3) << 14))
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -142,6 +144,12 @@ __device__ __forceinline__ int pinned(int v) {
 // context workload).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, uint32_t dst) {
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r), "{m0}"(dst) : "memory");
+}
+
+// The same load for data that other workgroups read too (the queries): a
+// temporal load, so the line stays in the L2 for them.
+__device__ __forceinline__ void dma16_shared(__amdgpu_buffer_rsrc_t r, int voff, uint32_t dst) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(dst) : "memory");
 }
 
 // bf16 pair -> fp16 pair (round to nearest even; exact inside the fp16 range)

@@ -11,7 +11,9 @@ kernels address the tile:
   contiguous LDS, its lanes fetch the chunks the layout puts there),
 * the Q.K^T fragment reads (128-bit, both kernels),
 * the dequantised stores of the fp8 / fp4 pieces (128-bit),
-* the transposed V reads of P.V (ds_read_b64_tr_b16, both kernels).
+* the transposed V reads of P.V (ds_read_b64_tr_b16, both kernels),
+* the bf16 kernel's query staging (direct-to-LDS loads of a wave's query
+  rows, half a row at a time, then B-operand fragment reads).
 
 LDS bank model: 64 banks of 4 bytes.  A 128-bit access is served 16 lanes at
 a time (16 x 16 B = one pass over the 64 banks), a 64-bit access 32 lanes at
@@ -148,3 +150,55 @@ def test_transposed_v_reads_address_the_right_elements_without_conflicts():
                     assert a == tile_off(tok, dim // 8) + (dim % 8) * 2
                     addrs.append(a)
                 assert _conflict_free(addrs, 32, 8), (ts, md, e)
+
+
+# bf16 kernel, query staging.  A wave's 32 query rows are 36 KiB of memory;
+# half h of them (bytes 576 h .. 576 h + 575 of every row) is 1152 chunks of
+# 16 bytes, chunk m = 36 r + k being byte 576 h + 16 k of row r.  Load c
+# writes LDS chunks 64 c .. 64 c + 63, lane l fetching memory chunk
+# 64 c + pi(l); fragment k-step ks (half ks // 18, j = ks % 18) of lane i is
+# row i & 31, bytes 32 ks + 16 (i >> 5) .. + 15, read from LDS chunk
+# slot(36 (i & 31) + 2 j + (i >> 5)).
+def _q_pi(x):
+    return x ^ ((x >> 4) & 3)
+
+
+def _q_slot(m):
+    return m ^ ((m >> 4) & 3)
+
+
+def test_query_staging_loads_place_each_chunk_once_where_the_reads_expect_it():
+    placed = {}
+    for c in range(18):
+        for lane in range(64):
+            m = 64 * c + _q_pi(lane)
+            assert m not in placed
+            placed[m] = 64 * c + lane
+            assert _q_slot(m) == 64 * c + lane
+    assert sorted(placed) == list(range(1152))
+
+
+def test_query_staging_loads_each_read_one_contiguous_kib_of_a_half():
+    for c in range(18):
+        chunks = sorted(64 * c + _q_pi(lane) for lane in range(64))
+        assert chunks == list(range(64 * c, 64 * c + 64))
+        for h in range(2):
+            lines = set()
+            for m in chunks:
+                r, k = divmod(m, 36)
+                lines.add((r * 1152 + 576 * h + 16 * k) // 128)
+            assert len(lines) <= 11, (c, h, len(lines))
+
+
+def test_query_fragment_reads_get_their_elements_without_conflicts():
+    for ks in range(D // 16):
+        h, j = divmod(ks, 18)
+        addrs = []
+        for i in range(64):
+            m = 36 * (i & 31) + 2 * j + (i >> 5)
+            # the chunk holds row m // 36, bytes 576 h + 16 (m % 36) of it
+            r, k = divmod(m, 36)
+            assert r == i & 31 and 576 * h + 16 * k == 32 * ks + 16 * (i >> 5)
+            addrs.append(16 * _q_slot(m))
+        assert max(addrs) < 18 * 1024
+        assert _conflict_free(addrs, 16, 16), ks
