@@ -11,18 +11,18 @@ recipe (a parity workload, or the sparse top-k one, whose step is the
 gathering decode, which reads the index lists itself, and the combine).
 
 Order of the run, all on one stream:
-  1. W warm-up steps (--warmup), then a pre-roll of further untimed steps
-     until at least --preroll-ms of GPU time has passed: the GPU needs tens
-     of milliseconds of load to reach its steady clock (reported as
-     "preroll_steps").
+  1. W warm-up steps (--warmup).
   2. Cold steps (--cold-steps): before each, a flush writes 1 GiB and then
      reads another 1 GiB, so no byte of the step's inputs is left in the L2s
      or the 256 MB last-level cache and no dirty line is left to write back;
      each step is timed alone by events around it (the flush is outside).
-     Five untimed steps follow, back to the warm state.
-  3. The timed region: exactly K steps (--steps) back to back, warm cache,
+  3. A pre-roll of untimed steps until at least --preroll-ms of GPU time has
+     passed: after a pause the GPU needs 30-40 ms of load to return to its
+     steady clock (kernels start ~20 % slower), so the pre-roll comes right
+     before the timed region (reported as "preroll_steps").
+  4. The timed region: exactly K steps (--steps) back to back, warm cache,
      bracketed by synchronisations: ``value`` and ``ms_per_step``.
-  4. A sampling pass of 8 x --kernel-samples more steps, every 8th of whose
+  5. A sampling pass of 8 x --kernel-samples more steps, every 8th of whose
      decode kernels is timed by HIP events recorded with its own dispatch
      (these cost ~6 us a step, so the timed region runs without them): the
      dominant kernel's roofline.
@@ -187,26 +187,6 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # pre-roll: untimed steps until --preroll-ms of GPU time has passed; the
-    # count comes from a first batch of 10, the rest is enqueued in one go
-    pre_steps, pre_ms = 0, 0.0
-    if args.preroll_ms > 0:
-        a, b = ev(), ev()
-        a.record(stream)
-        for _ in range(10):
-            step()
-        b.record(stream)
-        b.synchronize()
-        per = max(a.elapsed_time(b) / 10, 1e-3)
-        more = int(math.ceil(max(args.preroll_ms - a.elapsed_time(b), 0.0) / per))
-        c = ev()
-        for _ in range(more):
-            step()
-        c.record(stream)
-        c.synchronize()
-        pre_steps, pre_ms = 10 + more, a.elapsed_time(c)
-    print(f"[bench] pre-roll {pre_steps} steps, {pre_ms:.1f} ms", file=sys.stderr, flush=True)
-
     # cold steps: flush (write 1 GiB, then read another 1 GiB), then one step
     # timed alone; its decode kernel by dispatch events
     cold = None
@@ -232,8 +212,26 @@ def main():
             c_kern.append(k0.elapsed_time(k1))
         del flush_w, flush_r
         cold = (float(np.median(c_step)), float(np.median(c_kern)), len(c_step))
-        for _ in range(5):      # back to the warm state before the timed region
+
+    # pre-roll: untimed steps until --preroll-ms of GPU time has passed; the
+    # count comes from a first batch of 10, the rest is enqueued in one go
+    pre_steps, pre_ms = 0, 0.0
+    if args.preroll_ms > 0:
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(10):
             step()
+        b.record(stream)
+        b.synchronize()
+        per = max(a.elapsed_time(b) / 10, 1e-3)
+        more = int(math.ceil(max(args.preroll_ms - a.elapsed_time(b), 0.0) / per))
+        c = ev()
+        for _ in range(more):
+            step()
+        c.record(stream)
+        c.synchronize()
+        pre_steps, pre_ms = 10 + more, a.elapsed_time(c)
+    print(f"[bench] pre-roll {pre_steps} steps, {pre_ms:.1f} ms", file=sys.stderr, flush=True)
 
     # the timed region: K bare steps back to back
     t_start, t_stop = ev(), ev()
@@ -281,8 +279,10 @@ def main():
     k_gbs = kv_bytes / (kms * 1e-3) / 1e9
     k_tflops = fl / (kms * 1e-3) / 1e12
     # the kernel's roofline: HBM below the balance point (2.5 PFLOP/s over
-    # 8 TB/s = 312.5 flop/B), the matrix cores above it (the products run as
-    # 16-bit MFMA for both cache formats, so the 16-bit peak applies)
+    # 8 TB/s = 312.5 flop/B), the matrix cores above it.  The 16-bit peak
+    # applies to every cache format: P.V runs as 16-bit MFMA, and Q.K^T too
+    # except on the fp8 cache, where it runs as two block-scaled fp8
+    # products (q_hi, q_lo) at twice the rate, the time of one 16-bit product
     intensity = fl / kv_bytes
     if intensity <= BF16_MFMA_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
         roof = {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -305,7 +305,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3/e8m0 cache, fp16 mfma",
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3/e8m0 cache, fp8 (two-term query) + fp16 mfma",
                   "fp4": "fp4-e2m1/e8m0 cache, fp16 mfma"}[s.kv_dtype],
         "data": "synthetic (seeded N(0,1) cache and queries, DeepSeek-V3/R1 shapes)",
         "config": {"workload": s.name, "batch": s.batch, "s_q": s.s_q, "n_h": s.n_h, "d_c": s.d_c,

@@ -207,10 +207,11 @@ def _counters(args) -> str:
         simd_cycles = vals["GRBM_GUI_ACTIVE"] / args.xcds * args.cus * 4
         lines.append(f"  matrix cores busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {args.xcds} x {args.cus} CUs "
                      f"x 4 SIMDs) = {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.3f}")
-    mops = sum(vals.get(k, 0.0) for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16"))
+    kinds = [k for k in ("BF16", "F16", "F8", "F6F4") if f"SQ_INSTS_VALU_MFMA_MOPS_{k}" in vals]
+    mops = sum(vals[f"SQ_INSTS_VALU_MFMA_MOPS_{k}"] for k in kinds)
     if mops and "_duration_ns" in vals:
-        lines.append(f"  MFMA work = (MOPS_BF16 + MOPS_F16) x 512 flop = {mops * 512 / 1e9:.2f} GFLOP per dispatch; "
-                     f"over the dispatch duration {mops * 512 / vals['_duration_ns'] / 1e3:.1f} TFLOP/s")
+        lines.append(f"  MFMA work = ({' + '.join('MOPS_' + k for k in kinds)}) x 512 flop = {mops * 512 / 1e9:.2f} "
+                     f"GFLOP per dispatch; over the dispatch duration {mops * 512 / vals['_duration_ns'] / 1e3:.1f} TFLOP/s")
     if "SQ_LDS_BANK_CONFLICT" in vals and "SQ_LDS_IDX_ACTIVE" in vals and vals["SQ_LDS_IDX_ACTIVE"]:
         lines.append(f"  LDS bank-conflict cycles / LDS active cycles = "
                      f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_LDS_IDX_ACTIVE']:.4f}")
