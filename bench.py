@@ -47,7 +47,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
-FLOP_PER_ROW_TOKEN = 2 * 576 + 2 * 512   # Q.K^T over the 576-wide row + P.V over 512
+def flop_per_row_token(spec) -> int:
+    """Q.K^T over the d_c + d_R wide row, P.V over its d_c latent dims (2176 at 512 + 64)."""
+    return 2 * (spec.d_c + spec.d_r) + 2 * spec.d_c
 
 
 def parse():
@@ -71,15 +73,15 @@ def parse():
 
 
 def flops_per_step(w) -> int:
-    """2176 flop per (query row, token it attends to)."""
+    """2176 flop per (query row, token it attends to) at d_c = 512, d_R = 64."""
     s = w.spec
     if w.indices is not None:
-        return w.selected_tokens * s.n_h * FLOP_PER_ROW_TOKEN
+        return w.selected_tokens * s.n_h * flop_per_row_token(s)
     tot = 0
     for L in w.seq_lens.tolist():
         for j in range(s.s_q):
             tot += max(L - s.s_q + 1 + j, 0)
-    return tot * s.n_h * FLOP_PER_ROW_TOKEN
+    return tot * s.n_h * flop_per_row_token(s)
 
 
 def cpu_baseline(w, budget_s: float) -> dict:

@@ -81,7 +81,9 @@ typedef struct mla_decode_params {
     int32_t max_batch;          /* upper bound on the run-time batch, >= 1                  */
     int32_t s_q;                /* queries per sequence (1 = plain decode, 2 = MTP), 1..8   */
     int32_t n_h;                /* heads, a multiple of 32, <= 1024                         */
-    int32_t d_c;                /* latent width; this build: 512                            */
+    int32_t d_c;                /* latent width; this build: 512, or 448 with the FP8 cache
+                                   (D = 512: the record's own 528-byte row, constraint (2));
+                                   other widths give MLA_ERR_UNSUPPORTED                   */
     int32_t d_r;                /* RoPE key width; this build: 64                           */
     int32_t block_size;         /* tokens per page block: a power of two, 16..256 (64 is the
                                    usual size, 32 that of a ratio-2 compressed layer:

@@ -137,6 +137,10 @@ SPECS = {
     "sparse_fp8_topk2048_b64": WorkloadSpec("sparse_fp8_topk2048_b64", 64, ("uniform", 4096, 32768), topk=2048,
                                             kv_dtype="fp8", outlier_p=0.01, outlier_mult=20.0, seed=7),
 }
+# the record's own fp8 row ("DeepSeek-R1" record, constraint (2)): 512 dims
+# (d_c = 448 latent + 64 RoPE), 512 e4m3 codes + 16 e8m0 scales = 528 bytes,
+# no padding; the fp8_b64 recipe otherwise
+SPECS["fp8_b64_d512"] = dataclasses.replace(SPECS["fp8_b64"], name="fp8_b64_d512", d_c=448, seed=9)
 
 # reduced-size variants of the same recipes for element-by-element parity
 SPECS.update({
@@ -159,6 +163,12 @@ SPECS.update({
     "sparse_fp8_topk2048_b64_small": dataclasses.replace(SPECS["sparse_fp8_topk2048_b64"],
                                                          name="sparse_fp8_topk2048_b64_small", batch=5,
                                                          seq_lens=("uniform", 100, 3000), topk=700, spare_pages=8),
+    "fp8_b64_d512_small": dataclasses.replace(SPECS["fp8_b64_d512"], name="fp8_b64_d512_small", batch=5,
+                                              seq_lens=("uniform", 100, 2100), spare_pages=8),
+    "sparse_fp8_topk2048_b64_d512_small": dataclasses.replace(SPECS["sparse_fp8_topk2048_b64"],
+                                                              name="sparse_fp8_topk2048_b64_d512_small", batch=5,
+                                                              seq_lens=("uniform", 100, 3000), topk=700,
+                                                              spare_pages=8, d_c=448, seed=10),
 })
 
 # the long-context workload is the one the bandwidth target is stated on

@@ -40,6 +40,11 @@ constexpr int kMinQuota = 1;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// bytes of one query row's two e4m3 terms (the fp8 cache's decode)
+size_t qx_row_bytes(const mla_decode_handle* h) {
+    return 2 * mla_kv_row_stride(MLA_KV_FP8_E4M3_E8M0, h->p.d_c, h->p.d_r);
+}
+
 struct WsLayout {
     size_t seq_nsplit, seq_slot, part_lse, part_o, qx, total;
 };
@@ -51,10 +56,10 @@ WsLayout layout(const mla_decode_handle* h, int32_t batch) {
     l.seq_nsplit = off;    off += align_up(nb * sizeof(int32_t));
     l.seq_slot = off;      off += align_up(nb * sizeof(int32_t));
     l.part_lse = off;      off += align_up((size_t)h->partial_slots * h->rows * sizeof(float));
-    l.part_o = off;        off += align_up((size_t)h->partial_slots * h->rows * mla::kDc * sizeof(uint16_t));
+    l.part_o = off;        off += align_up((size_t)h->partial_slots * h->rows * h->p.d_c * sizeof(uint16_t));
     // fp8 cache: the queries as two e4m3 terms, written by the decode's first kernel
     l.qx = off;
-    if (h->p.kv_dtype == MLA_KV_FP8_E4M3_E8M0) off += align_up(nb * (size_t)h->rows * mla::kMxQxRowBytes);
+    if (h->p.kv_dtype == MLA_KV_FP8_E4M3_E8M0) off += align_up(nb * (size_t)h->rows * qx_row_bytes(h));
     l.total = off;
     return l;
 }
@@ -89,9 +94,9 @@ SparseLayout sparse_layout(const mla_decode_handle* h, int32_t batch, int32_t to
     l.seq_nsplit = off;  off += align_up(nu * sizeof(int32_t));
     l.seq_slot = off;    off += align_up(nu * sizeof(int32_t));
     l.part_lse = off;    off += align_up((size_t)l.slots * h->p.n_h * sizeof(float));
-    l.part_o = off;      off += align_up((size_t)l.slots * h->p.n_h * mla::kDc * sizeof(uint16_t));
+    l.part_o = off;      off += align_up((size_t)l.slots * h->p.n_h * h->p.d_c * sizeof(uint16_t));
     l.qx = off;
-    if (h->p.kv_dtype == MLA_KV_FP8_E4M3_E8M0) off += align_up(nu * (size_t)h->p.n_h * mla::kMxQxRowBytes);
+    if (h->p.kv_dtype == MLA_KV_FP8_E4M3_E8M0) off += align_up(nu * (size_t)h->p.n_h * qx_row_bytes(h));
     l.total = off;
     return l;
 }
@@ -122,6 +127,7 @@ mla::DecodeArgs decode_args(const mla_decode_handle* h, const void* q, const voi
     da.page_bytes = (int64_t)h->p.block_size * (int64_t)mla_kv_row_stride(h->p.kv_dtype, h->p.d_c, h->p.d_r);
     da.page_size = h->p.block_size;
     da.n_h = h->p.n_h;
+    da.d_c = h->p.d_c;
     da.max_blocks = h->p.max_blocks_per_seq;
     da.overhead_units = kOverheadUnits;
     da.min_quota = kMinQuota;
@@ -146,8 +152,11 @@ mla_status_t validate_params(const mla_decode_params_t* p) {
     if (p->num_workers < 0 || p->num_workers > mla::kMaxWorkers) return MLA_ERR_INVALID_ARGUMENT;
     if ((p->flags & ~MLA_FLAG_KV_WITHIN_4GIB) != 0) return MLA_ERR_INVALID_ARGUMENT;
     if ((p->d_c + p->d_r) % 32 != 0 && p->kv_dtype != MLA_KV_BF16) return MLA_ERR_INVALID_ARGUMENT;
-    // valid requests outside what this build instantiates
-    if (p->d_c != mla::kDc || p->d_r != mla::kDr) return MLA_ERR_UNSUPPORTED;
+    // valid requests outside what this build instantiates: d_r = 64 and
+    // d_c = 512, or d_c = 448 with the fp8 cache (the record's 528-byte row)
+    if (p->d_r != mla::kDr) return MLA_ERR_UNSUPPORTED;
+    if (p->d_c != mla::kDc && !(p->d_c == mla::kDcNarrow && p->kv_dtype == MLA_KV_FP8_E4M3_E8M0))
+        return MLA_ERR_UNSUPPORTED;
     if (p->block_size < 16 || p->block_size > 256 || (p->block_size & (p->block_size - 1)) != 0)
         return MLA_ERR_UNSUPPORTED;
     return MLA_OK;
@@ -306,6 +315,7 @@ mla_status_t mla_decode_run(mla_decode_handle_t h, const void* q, const void* kv
     ca.lse = lse;
     ca.batch = batch;
     ca.rows = h->rows;
+    ca.d_c = h->p.d_c;
     if (mla::launch_combine(ca, h->num_workers, stream) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
@@ -384,6 +394,7 @@ mla_status_t mla_decode_sparse_run(mla_decode_handle_t h, const void* q, const v
     ca.lse = lse;
     ca.batch = l.units;
     ca.rows = h->p.n_h;
+    ca.d_c = h->p.d_c;
     if (mla::launch_combine(ca, l.workers, stream) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }

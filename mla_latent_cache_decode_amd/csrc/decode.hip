@@ -148,7 +148,7 @@ struct Fp4Pieces {
 // pipeline's loads and LDS stores so that these issue between MFMAs.
 template <bool kSparse, typename QkHook, typename PvHook>
 __device__ __forceinline__ void compute_tile(const LDS_AS uint8_t* tile, const f16x8 (&qf)[kQRegSteps],
-                                             const LDS_AS uint8_t* qr, WaveState& st, int n_valid, uint64_t mask,
+                                             const LDS_AS uint8_t* qr, WaveState<>& st, int n_valid, uint64_t mask,
                                              float scale_log2, QkHook&& qk_hook, PvHook&& pv_hook) {
     const int lane = opaque_lane();
     const int hi = lane >> 5;
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_kernel(DecodeArg
         // head's softmax scale absorbs 2^sh
         f16x8 qf[kKSteps];      // the q_R part moves to LDS after the conversion
         float scale_lane;
-        WaveState st;
+        WaveState<> st;
         const int lane0 = tid & 63;
         // segment prologue, ordered for overlap: the first block-table
         // entries, then the first page as soon as its entry lands, then the

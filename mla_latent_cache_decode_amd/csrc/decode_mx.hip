@@ -18,13 +18,14 @@
 //
 // Mapping onto CDNA4 (one workgroup of 4 waves per CU, 160 KiB of LDS):
 //  * A first kernel writes the two-term query rows into the workspace, each
-//    term in the cache's own 608-byte row format.
-//  * Pages move HBM -> LDS raw (608-byte rows) with direct-to-LDS buffer
-//    loads, double buffered: page p + 1 is fetched while tile p is computed.
-//    In LDS a row is five 128-byte column blocks (the last one also holds the
-//    first 32 bytes of the next row, which are not used), token t's 16-byte
-//    chunk c at tile_off(t, c): conflict-free row reads.  Rows past the
-//    visible tokens are never fetched (the descriptor size excludes them).
+//    term in the cache's own row format.
+//  * Pages move HBM -> LDS raw (608-byte rows; 528 at the narrow latent
+//    width, see Fp8Dims) with direct-to-LDS buffer loads, double buffered:
+//    page p + 1 is fetched while tile p is computed.  In LDS a row is five
+//    128-byte column blocks (the last one also holds the first bytes of the
+//    next row, which are not used), token t's 16-byte chunk c at
+//    tile_off(t, c): conflict-free row reads.  Rows past the visible tokens
+//    are never fetched (the descriptor size excludes them).
 //  * Q.K^T: wave w owns query rows 32w .. 32w + 31; per 64-deep k-step and
 //    32-token block one K fragment (32 bytes per lane from the raw page) and
 //    its scale bytes feed two scaled MFMAs (q_hi, q_lo).  The latent part of
@@ -42,21 +43,35 @@ namespace mla {
 namespace {
 
 constexpr int kMxColBlocks = 5;                         // 128-byte column blocks of a raw row in LDS
-constexpr int kMxChunks = 8 * kMxColBlocks;             // 40 chunks of 16 bytes (608 + 32)
+constexpr int kMxChunks = 8 * kMxColBlocks;             // 40 chunks of 16 bytes (a row and some spare)
 constexpr int kMxRawBytes = kMxColBlocks * kPage * 128; // 40960: one raw page of 64 rows
-constexpr int kMxVtBytes = kPage * kDc * 2;             // 65536: the fp16 V tile
 constexpr int kMxQrBytes = 4096;                        // per wave: q_R fragments, 2 terms x 2 halves x 1 KiB
-constexpr int kLdsMx = 2 * kMxRawBytes + kMxVtBytes + 4 * kMxQrBytes;   // 163840 = all of a CU's LDS
 constexpr int kMxPiecesPerWave = 2 * kMxColBlocks;      // 10 pieces of 1 KiB: 16 tokens x 5 column blocks
-constexpr int kMxSteps = kD / 64;                       // 9 k-steps of 64 dims
-constexpr int kMxQRegSteps = kDc / 64;                  // 8 k-steps (the latent part) whose Q fragments live in VGPRs
-constexpr int kMxFrags = 2 * kMxSteps;                  // 18 K fragments per tile: (k-step, 32-token block)
-constexpr int kMxVPieces = kDc / 16 / 4;                // 8 V chunks of 16 codes per lane per tile
-constexpr int kMxScaleChunk = kD / 16;                  // 36: the chunk holding a row's first 16 scale bytes
 
-static_assert(kLdsMx == 163840, "the kernel takes all of a CU's LDS");
-static_assert(kFp8RowBytes + 32 == kMxChunks * 16, "five column blocks cover a row");
-static_assert(kMxQxRowBytes == 2 * kFp8RowBytes, "a query row is two cache-format rows");
+// Shapes per latent width DC (values at DC = 512 / 448)
+template <int DC>
+struct MxShape {
+    typedef Fp8Dims<DC> F;
+    static constexpr int kVtBytes = kPage * DC * 2;                         // 65536 / 57344: the fp16 V tile
+    static constexpr int kLds = 2 * kMxRawBytes + kVtBytes + 4 * kMxQrBytes;  // 163840 / 155648
+    static constexpr int kSteps = F::kD / 64;            // 9 / 8 k-steps of 64 dims
+    static constexpr int kQRegSteps = DC / 64;           // 8 / 7 k-steps (the latent part) whose Q fragments live in VGPRs
+    static constexpr int kFrags = 2 * kSteps;            // K fragments per tile: (k-step, 32-token block)
+    static constexpr int kVPieces = DC / 16 / 4;         // 8 / 7 V chunks of 16 codes per lane per tile
+    static constexpr int kScaleChunk = F::kD / 16;       // 36 / 32: the chunk holding a row's first 16 scale bytes
+    static constexpr bool kHiScales = F::kD / 32 > 16;   // scale bytes past the first 16 (D = 576: two)
+    // the last column block's chunks past the row (fetched from inside the
+    // row by the sparse gather, see dma_sparse): 38, 39 / 33 .. 39
+    static constexpr int kRowChunks = (F::kRowBytes + 15) / 16;
+    static constexpr int kSpareShift = kRowChunks == 38 ? 2 : 8;
+    static_assert(kLds <= 163840, "a CU's LDS");
+    static_assert(F::kRowBytes <= kMxChunks * 16 && F::kRowBytes > (kMxChunks - 8) * 16,
+                  "five column blocks cover a row");
+    static_assert(kRowChunks - kSpareShift >= 0 && kMxChunks - 1 - kSpareShift < kRowChunks,
+                  "spare chunks map inside the row");
+    static_assert(kScaleChunk * 16 == F::kD && (kHiScales || F::kD / 32 <= 16), "scales follow the codes");
+};
+static_assert(MxShape<kDc>::kLds == 163840, "the kernel takes all of a CU's LDS at 512 dims");
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -94,8 +109,11 @@ __device__ __forceinline__ void encode32(const float (&v)[32], int e, uint32_t (
 // its e8m0 scale; q_lo = the residual q - q_hi (exact in fp32) encoded the
 // same way.  Row r of qx holds q_hi's row (576 codes, 18 scales, padding)
 // then q_lo's, in the cache's row format.
+template <int DC>
 __global__ __launch_bounds__(256) void quantize_q_mx_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ qx,
                                                              int64_t rows) {
+    typedef Fp8Dims<DC> F;
+    constexpr int kD = F::kD;
     constexpr int kGroups = kD / 32;
     for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < rows * kGroups;
          gid += (int64_t)gridDim.x * blockDim.x) {
@@ -112,7 +130,7 @@ __global__ __launch_bounds__(256) void quantize_q_mx_kernel(const uint16_t* __re
                 v[8 * i + 2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xFFFF0000u);
             }
         }
-        uint8_t* dst = qx + row * kMxQxRowBytes;
+        uint8_t* dst = qx + row * F::kQxRowBytes;
 #pragma unroll
         for (int term = 0; term < 2; ++term) {
             float amax = 0.f;
@@ -121,10 +139,10 @@ __global__ __launch_bounds__(256) void quantize_q_mx_kernel(const uint16_t* __re
             const int e = e8m0_of(amax);
             uint32_t codes[8];
             encode32(v, e, codes);
-            u32x4* out = (u32x4*)(dst + term * kFp8RowBytes + 32 * g);
+            u32x4* out = (u32x4*)(dst + term * F::kRowBytes + 32 * g);
             out[0] = u32x4{codes[0], codes[1], codes[2], codes[3]};
             out[1] = u32x4{codes[4], codes[5], codes[6], codes[7]};
-            dst[term * kFp8RowBytes + kD + g] = (uint8_t)e;
+            dst[term * F::kRowBytes + kD + g] = (uint8_t)e;
             if (term == 0) {
                 // the residual of each value: q - decode(code) * 2^(e - 127)
                 static_for<0, 32>([&](auto i_c) {
@@ -206,12 +224,18 @@ __device__ __attribute__((aligned(256))) uint8_t g_sparse_zero_row[kSparseZeroRo
 // kWin (sparse only): the caller has declared that the whole cache lies in
 // the first kGatherWindow bytes from its base; rows are then gathered with
 // 32-bit buffer offsets.
-template <int PS, bool kSparse, bool kWin = false>
+template <int DC, int PS, bool kSparse, bool kWin = false>
 __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(DecodeArgs a) {
     typedef PageGeom<kSparse ? 16 : PS> Geom;
-    static_assert(kFp8RowBytes <= kSparseZeroRowBytes, "the zero row covers a row");
+    typedef MxShape<DC> X;
+    typedef Fp8Dims<DC> F;
+    constexpr int kD = F::kD;
+    constexpr int kRowBytes = F::kRowBytes;
+    constexpr int kMxQRegSteps = X::kQRegSteps, kMxFrags = X::kFrags, kMxVPieces = X::kVPieces;
+    constexpr int kMxScaleChunk = X::kScaleChunk;
+    static_assert(kRowBytes <= kSparseZeroRowBytes, "the zero row covers a row");
     static_assert(Geom::kRangeTok % 16 == 0, "a wave's 16 tokens lie in one page");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsMx];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[X::kLds];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
     int* sbuf = (int*)smem;                 // planner scratch; dead before the first page lands
 
@@ -232,7 +256,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
 
     LDS_AS uint8_t* const raws[2] = {lds, lds + kMxRawBytes};
     LDS_AS uint8_t* const vt = lds + 2 * kMxRawBytes;
-    LDS_AS uint8_t* const qr = lds + 2 * kMxRawBytes + kMxVtBytes + wave * kMxQrBytes;
+    LDS_AS uint8_t* const qr = lds + 2 * kMxRawBytes + X::kVtBytes + wave * kMxQrBytes;
     const int lane0 = tid & 63;
     // first token (within a tile) of the page this wave loads from; the
     // wave loads and dequantises tokens 16w .. 16w + 15
@@ -240,7 +264,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
     // direct-to-LDS source offset of this lane inside a piece: token i >> 3
     // of the piece's 8, the chunk whose swizzled slot is i & 7 (pieces of
     // odd token groups flip the slot's low bit: address ^ 16)
-    const int dma_lane = (lane0 >> 3) * kFp8RowBytes + (((lane0 & 7) ^ sw(lane0 >> 3)) << 4);
+    const int dma_lane = (lane0 >> 3) * kRowBytes + (((lane0 & 7) ^ sw(lane0 >> 3)) << 4);
 
     int64_t cost = start.cost;
     int slot_base = start.slot;
@@ -279,8 +303,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
             const int rows = __builtin_amdgcn_readfirstlane(
                 p < p_hi ? min(max(n_load - p * kPage - tok0, 0), Geom::kRangeTok) : 0);
             return make_rsrc(a.kv + (int64_t)__builtin_amdgcn_readfirstlane(phys) * a.page_bytes +
-                                 Geom::row_in_page(p, tok0) * kFp8RowBytes,
-                             rows * kFp8RowBytes);
+                                 Geom::row_in_page(p, tok0) * kRowBytes,
+                             rows * kRowBytes);
         };
         // piece k of this wave: token group g = 2 wave + (k & 1) (tokens
         // 8g .. 8g + 7), column block k >> 1; it lands at g * 1024 of that
@@ -288,8 +312,19 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
         auto dma_piece = [&](__amdgpu_buffer_rsrc_t r, LDS_AS uint8_t* buf, auto k_c) {
             constexpr int k = decltype(k_c)::value, gl = k & 1, cb = k >> 1;
             const int g = 2 * wave + gl;
-            const int off = (8 * g - tok0) * kFp8RowBytes + cb * 128;
-            dma16(r, (pinned(dma_lane) ^ (gl << 4)) + off, (uint32_t)(uintptr_t)(buf + cb * 8192 + g * 1024));
+            const int off = (8 * g - tok0) * kRowBytes + cb * 128;
+            int lane_off;
+            if constexpr (kRowBytes % 32 == 0) {
+                // the row part of dma_lane is a multiple of 32: bit 4 is the chunk's low bit
+                lane_off = pinned(dma_lane) ^ (gl << 4);
+            } else {
+                // a 528-byte stride moves bit 4 with the token: flip the chunk's low
+                // bit itself (+16 for an even chunk, -16 for an odd one)
+                const int l = opaque_lane();
+                const int flip = gl ? 16 - ((((l & 7) ^ sw(l >> 3)) & 1) << 5) : 0;
+                lane_off = pinned(dma_lane) + flip;
+            }
+            dma16(r, lane_off + off, (uint32_t)(uintptr_t)(buf + cb * 8192 + g * 1024));
         };
 
         // sparse gather plan.  Unit b is query position j of sequence b_seq;
@@ -343,23 +378,24 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
         const uint8_t* const zero_row = g_sparse_zero_row;
         // piece k of tile p (row ids rw): token 16w + 8 (k & 1) + (i >> 3),
         // column block k >> 1, as dma_piece.  The last column block's chunks
-        // 38 and 39 (the 32 bytes after a row, never read) are fetched from
-        // chunks 36 and 37 instead, so that no lane reads past its row.
+        // past the row (never read: 38 and 39 of a 608-byte row, 33 .. 39 of
+        // a 528-byte one) are fetched from chunks kSpareShift lower, inside
+        // the row, so that no lane reads past its row.
         auto dma_sparse = [&](const u32x2& rw, int p, LDS_AS uint8_t* buf, auto k_c) {
             constexpr int k = decltype(k_c)::value, gl = k & 1, cb = k >> 1;
             const uint32_t row = rw[gl];
             const bool live = p < p_hi && row != kNoRow;
             const int l = pinned(lane0);
             int c = (l & 7) ^ sw(l >> 3) ^ gl;
-            if constexpr (cb == kMxColBlocks - 1) c = c >= 6 ? c - 2 : c;
+            if constexpr (cb == kMxColBlocks - 1) c = 8 * cb + c >= X::kRowChunks ? c - X::kSpareShift : c;
             const int chunk = (cb * 8 + c) << 4;
             const uint32_t dst = (uint32_t)(uintptr_t)(buf + cb * 8192 + (2 * wave + gl) * 1024);
             if constexpr (kWin) {
-                constexpr uint32_t kRowMax = (kGatherWindow - kFp8RowBytes) / kFp8RowBytes;
+                constexpr uint32_t kRowMax = (kGatherWindow - kRowBytes) / kRowBytes;
                 const bool in = live && row <= kRowMax;
-                dma16(r_win, (int)(in ? row * (uint32_t)kFp8RowBytes + chunk : kGatherNone), dst);
+                dma16(r_win, (int)(in ? row * (uint32_t)kRowBytes + chunk : kGatherNone), dst);
             } else {
-                const uint8_t* base = live ? a.kv + (uint64_t)row * kFp8RowBytes : zero_row;
+                const uint8_t* base = live ? a.kv + (uint64_t)row * kRowBytes : zero_row;
                 dma16_gather((uint64_t)(base + chunk), dst);
             }
         };
@@ -386,38 +422,38 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
         }
         // this wave's 32 query rows, both terms, as MFMA B operands: lane i
         // holds row i & 31, chunks 4s + h and 4s + 2 + h (h = i >> 5) of
-        // k-step s; the RoPE step (s = 8) goes to LDS
+        // k-step s; the RoPE step (the last) goes to LDS
         i32x8 qf[2][kMxQRegSteps];
         MxScales qs[2];
         {
             const int h = lane0 >> 5;
             const int row = active ? row0 + (lane0 & 31) : row0;
-            const uint8_t* qrow = (const uint8_t*)a.qx + ((int64_t)b * M + (active ? row : 0)) * kMxQxRowBytes;
+            const uint8_t* qrow = (const uint8_t*)a.qx + ((int64_t)b * M + (active ? row : 0)) * F::kQxRowBytes;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
 #pragma unroll
                 for (int s = 0; s < kMxQRegSteps; ++s) {
-                    const u32x4 c0 = *(const u32x4*)(qrow + t * kFp8RowBytes + (4 * s + h) * 16);
-                    const u32x4 c1 = *(const u32x4*)(qrow + t * kFp8RowBytes + (4 * s + 2 + h) * 16);
+                    const u32x4 c0 = *(const u32x4*)(qrow + t * kRowBytes + (4 * s + h) * 16);
+                    const u32x4 c1 = *(const u32x4*)(qrow + t * kRowBytes + (4 * s + 2 + h) * 16);
                     qf[t][s] = i32x8{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3],
                                      (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
                 }
-                const u32x4 slo = *(const u32x4*)(qrow + t * kFp8RowBytes + kD);
-                const uint32_t shi = *(const uint32_t*)(qrow + t * kFp8RowBytes + kD + 16);
+                const u32x4 slo = *(const u32x4*)(qrow + t * kRowBytes + kD);
+                const uint32_t shi = X::kHiScales ? *(const uint32_t*)(qrow + t * kRowBytes + kD + 16) : 0u;
                 qs[t] = mx_scales(slo, shi, h);
                 // the previous segment's last tile has retired its q_R reads (barrier)
-                const u32x4 r0 = *(const u32x4*)(qrow + t * kFp8RowBytes + (4 * kMxQRegSteps + h) * 16);
-                const u32x4 r1 = *(const u32x4*)(qrow + t * kFp8RowBytes + (4 * kMxQRegSteps + 2 + h) * 16);
+                const u32x4 r0 = *(const u32x4*)(qrow + t * kRowBytes + (4 * kMxQRegSteps + h) * 16);
+                const u32x4 r1 = *(const u32x4*)(qrow + t * kRowBytes + (4 * kMxQRegSteps + 2 + h) * 16);
                 *(LDS_AS u32x4*)(qr + t * 2048 + lane0 * 16) = r0;
                 *(LDS_AS u32x4*)(qr + t * 2048 + 1024 + lane0 * 16) = r1;
             }
         }
-        WaveState st;
+        WaveState<F::kMdBlocks> st;
         st.m = -__builtin_inff();
         st.l = 0.f;
         st.o_zero = true;
 #pragma unroll
-        for (int md = 0; md < kMdBlocks; ++md) st.o[md] = f32x16{};
+        for (int md = 0; md < F::kMdBlocks; ++md) st.o[md] = f32x16{};
         __builtin_amdgcn_s_waitcnt(VMCNT0_IMM);
         __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
         wg_barrier();
@@ -464,7 +500,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
             for (int blk = 0; blk < 2; ++blk) {
                 const int t = 32 * blk + (lane & 31);
                 const u32x4 slo = *(const LDS_AS u32x4*)(raw + tile_off(t, kMxScaleChunk));
-                const uint32_t shi = *(const LDS_AS uint32_t*)(raw + tile_off(t, kMxScaleChunk + 1));
+                const uint32_t shi = X::kHiScales ? *(const LDS_AS uint32_t*)(raw + tile_off(t, kMxScaleChunk + 1)) : 0u;
                 ks[blk] = mx_scales(slo, shi, h);
             }
             // V dequantisation: lane i of wave w converts token 16w +
@@ -544,7 +580,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
             __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
             wg_barrier();
 
-            softmax_pv<kSparse>(vt, st, s0, s1, n_valid, mk_cur, a.scale_log2, lane, [](auto) {});
+            softmax_pv<kSparse, F::kMdBlocks>(vt, st, s0, s1, n_valid, mk_cur, a.scale_log2, lane, [](auto) {});
             if constexpr (kSparse) {
                 mk_cur = mk_next;
                 mk_next = mk_after;
@@ -559,42 +595,72 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
         // the last tile fetched page p_hi through a zero-size descriptor:
         // nothing was read and its zeros are never used
 
-        rowsplit_epilogue(a, st, lds + wave * (kRowsPerWave * 1024), b, M, row0, slot, active);
+        rowsplit_epilogue<F::kMdBlocks>(a, st, lds + wave * (kRowsPerWave * 1024), b, M, row0, slot, active);
         // the next segment's first page lands in these bytes
         __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
         wg_barrier();
     }
 }
 
+template <int DC>
+hipError_t launch_quantize_q_mx_dc(const DecodeArgs& a, hipStream_t stream) {
+    const int64_t rows = (int64_t)a.batch * a.s_q * a.n_h;
+    const int64_t threads = rows * (Fp8Dims<DC>::kD / 32);
+    const int64_t blocks = std::min<int64_t>((threads + 255) / 256, (int64_t)1 << 20);
+    hipLaunchKernelGGL(quantize_q_mx_kernel<DC>, dim3((unsigned)blocks), dim3(256), 0, stream, a.q, a.qx, rows);
+    return hipGetLastError();
+}
+
+template <int DC>
+hipError_t launch_decode_fp8_mx_dc(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
+                                   hipEvent_t ev_stop) {
+    const dim3 grid(a.num_workers * row_groups);
+    switch (a.page_size) {
+        case 16: return launch_with_events(mla_decode_mx_kernel<DC, 16, false>, grid, stream, ev_start, ev_stop, a);
+        case 32: return launch_with_events(mla_decode_mx_kernel<DC, 32, false>, grid, stream, ev_start, ev_stop, a);
+        case 64: return launch_with_events(mla_decode_mx_kernel<DC, 64, false>, grid, stream, ev_start, ev_stop, a);
+        case 128: return launch_with_events(mla_decode_mx_kernel<DC, 128, false>, grid, stream, ev_start, ev_stop, a);
+        case 256: return launch_with_events(mla_decode_mx_kernel<DC, 256, false>, grid, stream, ev_start, ev_stop, a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DC>
+hipError_t launch_decode_fp8_mx_sparse_dc(const DecodeArgs& a, int row_groups, hipStream_t stream,
+                                          hipEvent_t ev_start, hipEvent_t ev_stop, bool window) {
+    // rows are gathered one by one: the page-block size enters only as a shift
+    const dim3 grid(a.num_workers * row_groups);
+    return window ? launch_with_events(mla_decode_mx_kernel<DC, 64, true, true>, grid, stream, ev_start, ev_stop, a)
+                  : launch_with_events(mla_decode_mx_kernel<DC, 64, true, false>, grid, stream, ev_start, ev_stop, a);
+}
+
 }  // namespace
 
 hipError_t launch_quantize_q_mx(const DecodeArgs& a, hipStream_t stream) {
-    const int64_t rows = (int64_t)a.batch * a.s_q * a.n_h;
-    const int64_t threads = rows * (kD / 32);
-    const int64_t blocks = std::min<int64_t>((threads + 255) / 256, (int64_t)1 << 20);
-    hipLaunchKernelGGL(quantize_q_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.q, a.qx, rows);
-    return hipGetLastError();
+    switch (a.d_c) {
+        case kDc: return launch_quantize_q_mx_dc<kDc>(a, stream);
+        case kDcNarrow: return launch_quantize_q_mx_dc<kDcNarrow>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_decode_fp8_mx(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                                 hipEvent_t ev_stop) {
-    const dim3 grid(a.num_workers * row_groups);
-    switch (a.page_size) {
-        case 16: return launch_with_events(mla_decode_mx_kernel<16, false>, grid, stream, ev_start, ev_stop, a);
-        case 32: return launch_with_events(mla_decode_mx_kernel<32, false>, grid, stream, ev_start, ev_stop, a);
-        case 64: return launch_with_events(mla_decode_mx_kernel<64, false>, grid, stream, ev_start, ev_stop, a);
-        case 128: return launch_with_events(mla_decode_mx_kernel<128, false>, grid, stream, ev_start, ev_stop, a);
-        case 256: return launch_with_events(mla_decode_mx_kernel<256, false>, grid, stream, ev_start, ev_stop, a);
+    switch (a.d_c) {
+        case kDc: return launch_decode_fp8_mx_dc<kDc>(a, row_groups, stream, ev_start, ev_stop);
+        case kDcNarrow: return launch_decode_fp8_mx_dc<kDcNarrow>(a, row_groups, stream, ev_start, ev_stop);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_decode_fp8_mx_sparse(const DecodeArgs& a, int row_groups, hipStream_t stream, hipEvent_t ev_start,
                                        hipEvent_t ev_stop, bool window) {
-    // rows are gathered one by one: the page-block size enters only as a shift
-    const dim3 grid(a.num_workers * row_groups);
-    return window ? launch_with_events(mla_decode_mx_kernel<64, true, true>, grid, stream, ev_start, ev_stop, a)
-                  : launch_with_events(mla_decode_mx_kernel<64, true, false>, grid, stream, ev_start, ev_stop, a);
+    switch (a.d_c) {
+        case kDc: return launch_decode_fp8_mx_sparse_dc<kDc>(a, row_groups, stream, ev_start, ev_stop, window);
+        case kDcNarrow:
+            return launch_decode_fp8_mx_sparse_dc<kDcNarrow>(a, row_groups, stream, ev_start, ev_stop, window);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace mla

@@ -1,9 +1,10 @@
 // Row-split softmax and P.V shared by the quantised-cache decode kernels
 // ("DeepSeek R1 Architecture & Deployment Guide", section 1.1: softmax of the
 // scores over the context, then the softmax-weighted sum of the latent rows).
-// Each wave owns 32 query rows and their O^T accumulator (512 dims x 32 rows,
-// 256 AGPRs); its S^T scores (two 32-token blocks) are the B operand of P.V
-// after the softmax, so no weights are exchanged between waves.
+// Each wave owns 32 query rows and their O^T accumulator (MD blocks of 32
+// dims x 32 rows: 512 dims, 256 AGPRs, or 448 for the fp8 cache's narrow
+// row); its S^T scores (two 32-token blocks) are the B operand of P.V after
+// the softmax, so no weights are exchanged between waves.
 #pragma once
 
 #include "decode_common.h"
@@ -11,14 +12,16 @@
 namespace mla {
 namespace {
 
-constexpr int kPvSteps = 4 * kMdBlocks;         // 64 MFMA steps for P.V
+constexpr int kPvSteps = 4 * kMdBlocks;         // 64 MFMA steps for P.V at 512 dims
 constexpr float kRescaleTau = 15.0f;            // log2 units: p <= 2^15 stays inside fp16
 constexpr int kPvAhead = 2;                     // V fragment prefetch distance (steps)
 constexpr int kPMakeAt = 6;                     // P.V step (within a 16-step block) that builds the next P fragment
 
-// per-wave state of the online softmax and the O accumulator
+// per-wave state of the online softmax and the O accumulator (MD blocks of
+// 32 dims)
+template <int MD = kMdBlocks>
 struct WaveState {
-    f32x16 o[kMdBlocks];     // O^T accumulator: dims x heads
+    f32x16 o[MD];            // O^T accumulator: dims x heads
     float m;                 // running max (log2 units, lane's head)
     float l;                 // partial sum of exp over this lane's half of the tokens
     bool o_zero;             // nothing accumulated yet (wave-uniform)
@@ -32,9 +35,10 @@ struct WaveState {
 // token t).  Lazy rescaling: the running max is raised only when the tile's
 // max exceeds it by more than kRescaleTau, and O is then rescaled in place.
 // `lane` is the caller's opaque_lane().
-template <bool kSparse, typename PvHook>
-__device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveState& st, f32x16& s0, f32x16& s1,
+template <bool kSparse, int MD = kMdBlocks, typename PvHook>
+__device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveState<MD>& st, f32x16& s0, f32x16& s1,
                                            int n_valid, uint64_t mask, float scale_log2, int lane, PvHook&& pv_hook) {
+    constexpr int kSteps = 4 * MD;              // P.V MFMA steps: 4 token blocks x MD dim blocks
     const int hi = lane >> 5;
     const LDS_AS uint8_t* tile = vtile;
 
@@ -68,7 +72,7 @@ __device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveStat
         if (!st.o_zero) {
             const float alpha = need ? fast_exp2(st.m - m_new) : 1.0f;
 #pragma unroll
-            for (int md = 0; md < kMdBlocks; ++md) {
+            for (int md = 0; md < MD; ++md) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) st.o[md][r] = scale_acc(st.o[md][r], alpha);
             }
@@ -98,7 +102,7 @@ __device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveStat
     f16x8 pf[4];
     pf[0] = make_p(std::integral_constant<int, 0>{});
 
-    // ---- O^T += V^T P^T.  Step s covers (kb = s >> 4, md = s & 15); its V^T
+    // ---- O^T += V^T P^T.  Step s covers (kb = s / MD, md = s % MD); its V^T
     // fragment is two transposed reads (tokens kb*16 + e4*8 + tok_lane, dims
     // md*32 + dim_lane), issued kPvAhead steps ahead into rotating buffers.
     __builtin_amdgcn_sched_barrier(0);
@@ -121,29 +125,29 @@ __device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveStat
     f16x8 vf[kVBufs];
     auto read_v = [&](auto step_c) -> f16x8 {
         constexpr int step = decltype(step_c)::value;
-        constexpr int kb_ = step >> 4, md = step & 15;
+        constexpr int kb_ = step / MD, md = step % MD;
         constexpr int off = (md >> 1) * 8192 + kb_ * 16 * 128;
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][0] + off));
         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][1] + off));
         return __builtin_bit_cast(f16x8, i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
     };
     static_for<0, kPvAhead>([&](auto i) { vf[decltype(i)::value] = read_v(i); });
-    static_for<0, kPvSteps>([&](auto step_c) {
+    static_for<0, kSteps>([&](auto step_c) {
         constexpr int step = decltype(step_c)::value;
-        if constexpr (step + kPvAhead < kPvSteps)
+        if constexpr (step + kPvAhead < kSteps)
             vf[(step + kPvAhead) % kVBufs] = read_v(std::integral_constant<int, step + kPvAhead>{});
-        st.o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[step % kVBufs], pf[step >> 4], st.o[step & 15],
+        st.o[step % MD] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[step % kVBufs], pf[step / MD], st.o[step % MD],
                                                                   0, 0, 0);
         // VALU and memory work issues while the MFMA runs
-        if constexpr ((step & 15) == kPMakeAt && (step >> 4) < 3)
-            pf[(step >> 4) + 1] = make_p(std::integral_constant<int, (step >> 4) + 1>{});
+        if constexpr ((step % MD) == kPMakeAt && (step / MD) < 3)
+            pf[(step / MD) + 1] = make_p(std::integral_constant<int, (step / MD) + 1>{});
         pv_hook(step_c);
         __builtin_amdgcn_sched_barrier(0);
     });
     // keep the accumulator's home in AGPRs (it is only touched by MFMA in the
     // steady state); VALU users copy out and back
 #pragma unroll
-    for (int md = 0; md < kMdBlocks; ++md) asm volatile("" : "+a"(st.o[md]));
+    for (int md = 0; md < MD; ++md) asm volatile("" : "+a"(st.o[md]));
     st.l += lsum;
     st.o_zero = false;
 }
@@ -157,8 +161,10 @@ __device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveStat
 // stored directly, every instruction scatters 16 bytes over 32 rows
 // (fp8_b64: 199.9 -> 191.0 us per decode with the staging).  Callers place a
 // workgroup barrier before the staged bytes are reused.
-__device__ __forceinline__ void rowsplit_epilogue(const DecodeArgs& a, const WaveState& st, LDS_AS uint8_t* stage,
+template <int MD = kMdBlocks>
+__device__ __forceinline__ void rowsplit_epilogue(const DecodeArgs& a, const WaveState<MD>& st, LDS_AS uint8_t* stage,
                                                   int b, int M, int row0, int slot, bool active) {
+    constexpr int DC = 32 * MD;                 // dims of an output row
     if (!active) return;
     const int lane = opaque_lane();
     const float l_tot = pair_sum(st.l);
@@ -168,9 +174,9 @@ __device__ __forceinline__ void rowsplit_epilogue(const DecodeArgs& a, const Wav
     const int row = row0 + (lane & 31);
     const int hi = lane >> 5;
     if (slot < 0) {
-        float* dst = a.out + ((int64_t)b * M + row) * kDc + hi * 4;
+        float* dst = a.out + ((int64_t)b * M + row) * DC + hi * 4;
 #pragma unroll
-        for (int md = 0; md < kMdBlocks; ++md) {
+        for (int md = 0; md < MD; ++md) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const f32x4 v = {st.o[md][r4 * 4 + 0] * inv, st.o[md][r4 * 4 + 1] * inv, st.o[md][r4 * 4 + 2] * inv,
@@ -183,7 +189,7 @@ __device__ __forceinline__ void rowsplit_epilogue(const DecodeArgs& a, const Wav
     }
     const int r = lane & 31;
 #pragma unroll
-    for (int md = 0; md < kMdBlocks; ++md) {
+    for (int md = 0; md < MD; ++md) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const f16x4 h = {(_Float16)(st.o[md][r4 * 4 + 0] * inv), (_Float16)(st.o[md][r4 * 4 + 1] * inv),
@@ -194,12 +200,14 @@ __device__ __forceinline__ void rowsplit_epilogue(const DecodeArgs& a, const Wav
     }
     if (lane < 32) a.plan.part_lse[(int64_t)row * a.plan.slots + slot] = lse_v;
     __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
-    // row j of this wave: lane l stores logical slots 2l, 2l + 1
-    uint16_t* const pbase = a.plan.part_o + ((int64_t)slot * M + row0) * kDc + lane * 8;
+    // row j of this wave: lane l stores logical slots 2l, 2l + 1 (lanes
+    // past the row's DC / 8 have nothing to store)
+    if (4 * MD < 64 && lane >= 4 * MD) return;
+    uint16_t* const pbase = a.plan.part_o + ((int64_t)slot * M + row0) * DC + lane * 8;
     for (int j = 0; j < kRowsPerWave; ++j) {
         u32x4 v = *(const LDS_AS u32x4*)(stage + j * 1024 + (((2 * lane) ^ (j & 30)) << 3));
         if (j & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        *(u32x4*)(pbase + j * kDc) = v;
+        *(u32x4*)(pbase + j * DC) = v;
     }
 }
 

@@ -26,6 +26,20 @@ constexpr int kFp4Payload = kD / 2 + kD / 16;                // 324
 constexpr int kFp4RowBytes = (kFp4Payload + 15) / 16 * 16;  // 336
 // the fp8 decode's query rows: two terms (q_hi, q_lo), each in the fp8 row format
 constexpr int kMxQxRowBytes = 2 * kFp8RowBytes;             // 1216
+// The fp8 cache also serves a latent width of 448 (D = 512): the "DeepSeek-R1"
+// record's constraint (2) row, 512 e4m3 codes and 16 e8m0 scales = 528 bytes
+// with no padding.  Per latent width DC: the row, its stride, the 32-dim
+// output blocks, the two-term query row.
+constexpr int kDcNarrow = 448;
+template <int DC>
+struct Fp8Dims {
+    static constexpr int kDc = DC;
+    static constexpr int kD = DC + kDr;                             // 576 / 512
+    static constexpr int kRowBytes = (kD + kD / 32 + 15) / 16 * 16;  // 608 / 528
+    static constexpr int kMdBlocks = DC / 32;                        // 16 / 14
+    static constexpr int kQxRowBytes = 2 * kRowBytes;
+};
+static_assert(Fp8Dims<kDc>::kRowBytes == kFp8RowBytes && Fp8Dims<kDcNarrow>::kRowBytes == 528, "fp8 rows");
 constexpr int kRowsPerGroup = 128;            // query rows one workgroup serves
 constexpr int kRowsPerWave = 32;
 constexpr int kDecodeThreads = 256;           // 4 waves of 64
@@ -40,7 +54,7 @@ struct PlanView {
     int32_t* seq_nsplit;        // [batch]
     int32_t* seq_slot;          // [batch]
     float* part_lse;            // [M][slots]: one row's split LSEs are contiguous
-    uint16_t* part_o;           // fp16 [slots][M][kDc]: a split's O / l
+    uint16_t* part_o;           // fp16 [slots][M][d_c]: a split's O / l
     int32_t slots;              // partial slot capacity (row stride of part_lse)
 };
 
@@ -49,10 +63,10 @@ struct DecodeArgs {
     const uint8_t* kv;          // pages
     const int32_t* block_table; // [B][max_blocks]
     const int32_t* seq_lens;    // [B]
-    float* out;                 // [B][M][kDc]
+    float* out;                 // [B][M][d_c]
     float* lse;                 // [B][M] or null
     PlanView plan;
-    uint8_t* qx;                // fp8 cache: the two-term query rows [B][M][kMxQxRowBytes] (workspace)
+    uint8_t* qx;                // fp8 cache: the two-term query rows [B][M][2 fp8 rows] (workspace)
     int64_t page_bytes;         // bytes per page
     int32_t page_size;          // tokens per page block (16 .. 256, a power of two)
     int32_t batch;
@@ -71,6 +85,7 @@ struct DecodeArgs {
     int32_t sparse_topk;
     const int32_t* sparse_indices;  // [units][topk] token positions
     int32_t sparse_sq;              // query positions per sequence (unit u = b * sparse_sq + j)
+    int32_t d_c;                    // latent width: kDc, or kDcNarrow (fp8 cache only)
 };
 
 // A sparse entry that does not take part has no row (row ids are
@@ -94,6 +109,7 @@ struct CombineArgs {
     float* lse;                 // may be null
     int32_t batch;
     int32_t rows;               // M = s_q * n_h
+    int32_t d_c;                // latent width of a row (a multiple of 8, at most kDc)
 };
 
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.

@@ -20,7 +20,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // A block merges RPB rows; each row's splits are dealt to WPR waves in
 // contiguous ranges (WPR = 8, RPB = 1 for few long sequences with many
 // splits; WPR = 1, RPB = 4 when sequences have few splits).  A lane owns 8
-// dims of the row: one 16-byte fp16 load per split.
+// dims of the row: one 16-byte fp16 load per split (rows of d_c <= 512 dims;
+// lanes past d_c / 8 idle).
 //
 // Latency is the cost to beat: the whole merge is one round of loads.  Each
 // wave issues the row's split LSEs and its first kLoadBatch partial rows
@@ -63,11 +64,13 @@ __device__ __forceinline__ void acc_add(f32x4 (&acc)[2], float w, const f16x8& h
 
 __device__ __forceinline__ void store_row(const CombineArgs& a, int b, int row, int t, const f32x4 (&acc)[2],
                                           float mx, float sum) {
-    float* o = a.out + ((int64_t)b * a.rows + row) * kDc + t * 8;
+    float* o = a.out + ((int64_t)b * a.rows + row) * a.d_c + t * 8;
     const bool dead = !(sum > 0.f);                       // no visible token (or no split)
     const float inv = dead ? 0.f : 1.0f / sum;
-    *(f32x4*)o = acc[0] * inv;
-    *(f32x4*)(o + 4) = acc[1] * inv;
+    if (t * 8 < a.d_c) {
+        *(f32x4*)o = acc[0] * inv;
+        *(f32x4*)(o + 4) = acc[1] * inv;
+    }
     if (a.lse && t == 0) a.lse[(int64_t)b * a.rows + row] = dead ? -__builtin_inff() : mx + logf(sum);
 }
 
@@ -96,14 +99,17 @@ __global__ __launch_bounds__(WPR * RPB * 64) void combine_kernel(CombineArgs a) 
     const int base = a.plan.seq_slot[b];
     const int per = (n + WPR - 1) / WPR;
     const int lo = min(part * per, n), hi = min(lo + per, n);
-    const uint32_t stride = (uint32_t)M * kDc * 2;        // bytes between split slots of a row
+    const uint32_t stride = (uint32_t)M * a.d_c * 2;      // bytes between split slots of a row
+    // a lane past the row's d_c / 8 loads from past the descriptor's range:
+    // zeros, no memory touched (its sums are not stored)
+    const uint32_t t_off = t * 8 < a.d_c ? (uint32_t)t * 16 : 0x80000000u;
     const float* const lse_row = a.plan.part_lse + (int64_t)row * a.plan.slots + base;
     const __amdgpu_buffer_rsrc_t r_lse = make_rsrc(lse_row, (uint32_t)n * 4);
     const __amdgpu_buffer_rsrc_t r_own = make_rsrc(lse_row + lo, (uint32_t)(hi - lo) * 4);
     // partial rows of this wave's splits j .. j + kLoadBatch - 1 (one
     // descriptor per batch keeps every offset far inside 32 bits)
     auto batch_rsrc = [&](int j) {
-        return make_rsrc(a.plan.part_o + ((int64_t)(base + lo + j) * M + row) * kDc,
+        return make_rsrc(a.plan.part_o + ((int64_t)(base + lo + j) * M + row) * a.d_c,
                          (uint32_t)max(min(kLoadBatch, hi - lo - j), 0) * stride);
     };
 
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(WPR * RPB * 64) void combine_kernel(CombineArgs a) 
     {
         const __amdgpu_buffer_rsrc_t r_o = batch_rsrc(0);
 #pragma unroll
-        for (int u = 0; u < kLoadBatch; ++u) v[u] = load_row8(r_o, u * stride + t * 16);
+        for (int u = 0; u < kLoadBatch; ++u) v[u] = load_row8(r_o, u * stride + t_off);
     }
     l_a = t < n ? l_a : ninf;
     l_b = 64 + t < n ? l_b : ninf;
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(WPR * RPB * 64) void combine_kernel(CombineArgs a) 
             if (c > 0 || i > 0) {                         // the first batch is already loaded
                 const __amdgpu_buffer_rsrc_t r_o = batch_rsrc(c + i);
 #pragma unroll
-                for (int u = 0; u < kLoadBatch; ++u) v[u] = load_row8(r_o, u * stride + t * 16);
+                for (int u = 0; u < kLoadBatch; ++u) v[u] = load_row8(r_o, u * stride + t_off);
             }
 #pragma unroll
             for (int u = 0; u < kLoadBatch; ++u) {

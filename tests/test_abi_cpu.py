@@ -96,7 +96,10 @@ def _init(**over):
     (dict(flags=4), 1),
     (dict(flags=2), 1),          # only MLA_FLAG_KV_WITHIN_4GIB is defined
     (dict(flags=-1), 1),
-    (dict(d_c=448), 2),          # valid request, not instantiated in this build
+    (dict(d_c=448), 2),          # valid request, instantiated for the fp8 cache only
+    (dict(d_c=448, kv_dtype="fp4"), 2),
+    (dict(d_c=384, kv_dtype="fp8"), 2),
+    (dict(d_c=448, d_r=0, kv_dtype="fp8"), 2),
     (dict(block_size=48), 2),    # page blocks: powers of two from 16 to 256
     (dict(block_size=8), 2),
     (dict(block_size=512), 2),
@@ -129,6 +132,15 @@ def test_valid_params_without_a_gpu_report_hip_error(block_size, flags):
     if torch.cuda.is_available():
         pytest.skip("this host has a GPU")
     st, h = _init(block_size=block_size, flags=flags)
+    assert st == 4 and h is None
+
+
+def test_fp8_narrow_row_passes_host_validation():
+    # d_c = 448, d_r = 64: the record's 528-byte fp8 row
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("this host has a GPU")
+    st, h = _init(d_c=448, kv_dtype="fp8")
     assert st == 4 and h is None
 
 

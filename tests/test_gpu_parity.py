@@ -15,7 +15,7 @@ from gpu_helpers import run_gpu, oracle, assert_parity, make_decoder, say
 pytestmark = pytest.mark.gpu
 
 SMALL = ["single_1k_small", "paged_b32_small", "long_ctx_b4_small", "fp8_b64_small", "mtp2_b128_small",
-         "fp4_b64_small"]
+         "fp4_b64_small", "fp8_b64_d512_small"]
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -43,6 +43,7 @@ FULL_SAMPLES = {
     "fp8_b64": [0, 33, 63],
     "mtp2_b128": [0, 64, 127],
     "fp4_b64": [0, 33, 63],
+    "fp8_b64_d512": [0, 33, 63],
 }
 
 
@@ -75,7 +76,7 @@ def _identity_layout(w):
     return dataclasses.replace(w, pool=pool2, block_table=bt2)
 
 
-@pytest.mark.parametrize("name", ["paged_b32_small", "fp8_b64_small", "mtp2_b128_small"])
+@pytest.mark.parametrize("name", ["paged_b32_small", "fp8_b64_small", "mtp2_b128_small", "fp8_b64_d512_small"])
 def test_paged_equals_identity_bitwise(name):
     w = make_workload(name)
     w2 = _identity_layout(w)
@@ -122,7 +123,7 @@ def _repage(w, page: int, seed: int):
 
 
 @pytest.mark.parametrize("name", ["paged_b32_small", "fp8_b64_small", "mtp2_b128_small", "long_ctx_b4_small",
-                                  "fp4_b64_small"])
+                                  "fp4_b64_small", "fp8_b64_d512_small"])
 @pytest.mark.parametrize("page", [16, 32, 128, 256])
 def test_page_block_sizes(name, page):
     # page blocks other than 64 ("DeepSeek-R1" record, constraint (1): 32 for

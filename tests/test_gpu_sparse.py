@@ -50,6 +50,8 @@ VARIANTS = [
     dataclasses.replace(SPECS["sparse_fp8_topk2048_b64_small"], name="sparse_fp8_mtp2_small", s_q=2, seed=50),
     dataclasses.replace(SPECS["sparse_fp8_topk2048_b64_small"], name="sparse_fp8_page32_small", page=32, seed=51),
     dataclasses.replace(SPECS["sparse_fp8_topk2048_b64_small"], name="sparse_fp4_small", kv_dtype="fp4", seed=54),
+    # the record's 528-byte fp8 row (d_c = 448)
+    SPECS["sparse_fp8_topk2048_b64_d512_small"],
     # flat softmax: a token wrongly counted or dropped by the tile mask moves
     # the output by about 1/n (the lists here are shorter than 64 tokens past
     # the last full tile, both tile halves partly valid)
@@ -118,13 +120,14 @@ def test_sparse_reads_only_selected_rows(kv_dtype):
     np.testing.assert_array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "fp4"])
-def test_sparse_over_whole_context_equals_dense_bitwise(kv_dtype):
+@pytest.mark.parametrize("kv_dtype,d_c", [("bf16", 512), ("fp8", 512), ("fp4", 512), ("fp8", 448)],
+                         ids=["bf16", "fp8", "fp4", "fp8_d512"])
+def test_sparse_over_whole_context_equals_dense_bitwise(kv_dtype, d_c):
     # index lists 0 .. L-1 in order (padded with -1) visit the dense decode's
     # tiles in the dense order; with one worker neither run splits, so the
     # two must agree bit for bit
-    spec = WorkloadSpec(f"sparse_vs_dense_{kv_dtype}", 3, ("fixed", (700, 64, 1500)), topk=1500, spare_pages=4,
-                        seed=49, kv_dtype=kv_dtype, outlier_p=0.01, outlier_mult=20.0)
+    spec = WorkloadSpec(f"sparse_vs_dense_{kv_dtype}_{d_c}", 3, ("fixed", (700, 64, 1500)), topk=1500,
+                        spare_pages=4, seed=49, kv_dtype=kv_dtype, outlier_p=0.01, outlier_mult=20.0, d_c=d_c)
     w = make_workload(spec)
     idx = np.full_like(w.indices, -1)
     for b in range(spec.batch):

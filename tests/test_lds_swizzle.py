@@ -101,6 +101,36 @@ def test_qk_fragment_reads_are_conflict_free(blk):
         assert _conflict_free(addrs, 16, 16), ks
 
 
+def _mx_lane_off(lane, gl, row_bytes):
+    # the block-scaled fp8 kernel's page loads: lane i of a piece fetches
+    # token i >> 3 of the piece's 8, chunk ((i & 7) ^ sw(i >> 3)) of the
+    # column block, with the chunk's low bit flipped for odd token groups
+    # (gl = 1): an XOR of the whole offset when the row stride is a multiple
+    # of 32, else +16 / -16 by the chunk's parity
+    c0 = (lane & 7) ^ sw(lane >> 3)
+    base = (lane >> 3) * row_bytes + (c0 << 4)
+    if row_bytes % 32 == 0:
+        return base ^ (gl << 4)
+    return base + ((16 - ((c0 & 1) << 5)) if gl else 0)
+
+
+@pytest.mark.parametrize("row_bytes", [608, 528])
+def test_fp8_page_loads_write_their_own_chunks(row_bytes):
+    # piece k of wave w (page-block size >= 64): token group g = 2w + (k & 1),
+    # column block k >> 1; LDS bytes cb * 8192 + g * 1024 + 16 i; five column
+    # blocks of 8 chunks hold a row (608 or 528 bytes) and spare chunks
+    for wave in range(4):
+        for k in range(10):
+            gl, cb = k & 1, k >> 1
+            g = 2 * wave + gl
+            for i in range(64):
+                src = 8 * g * row_bytes + cb * 128 + _mx_lane_off(i, gl, row_bytes)
+                t = 8 * g + (i >> 3)
+                byte = src - t * row_bytes
+                assert byte % 16 == 0 and 0 <= byte < 640, (wave, k, i, byte)
+                assert tile_off(t, byte // 16) == cb * 8192 + g * 1024 + 16 * i
+
+
 def test_dequantised_piece_stores_are_conflict_free():
     # fp8 / fp4 piece k of wave w: lane i stores token 16w + (i & 15), chunks
     # 2 (4k + (i >> 4)) + c (c = 0, 1, one 128-bit store each)

@@ -25,9 +25,9 @@ from oracle import mla, unabsorbed, brute, formats
 from mla_inputs import WorkloadSpec, make_workload
 
 
-def _tiny_spec(kv_dtype, s_q, seed, lens=(1, 64, 65, 130), n_h=2):
-    return WorkloadSpec(f"tiny_{kv_dtype}_{s_q}", len(lens), ("fixed", tuple(lens)), kv_dtype=kv_dtype,
-                        s_q=s_q, n_h=n_h, spare_pages=3, seed=seed,
+def _tiny_spec(kv_dtype, s_q, seed, lens=(1, 64, 65, 130), n_h=2, d_c=512):
+    return WorkloadSpec(f"tiny_{kv_dtype}_{s_q}_{d_c}", len(lens), ("fixed", tuple(lens)), kv_dtype=kv_dtype,
+                        s_q=s_q, n_h=n_h, spare_pages=3, seed=seed, d_c=d_c,
                         outlier_p=0.05 if kv_dtype != "bf16" else 0.0, outlier_mult=20.0)
 
 
@@ -41,8 +41,9 @@ def _run_oracle(w, **kw):
 # the pins, written as functions so the mutation test can re-run them
 # ----------------------------------------------------------------------------
 
-def pin_brute_force(kv_dtype, s_q):
-    w = make_workload(_tiny_spec(kv_dtype, s_q, seed=100 + s_q + {"bf16": 0, "fp8": 7, "fp4": 13}[kv_dtype]))
+def pin_brute_force(kv_dtype, s_q, d_c=512):
+    w = make_workload(_tiny_spec(kv_dtype, s_q, seed=100 + s_q + {"bf16": 0, "fp8": 7, "fp4": 13}[kv_dtype]
+                                 + (0 if d_c == 512 else 50), d_c=d_c))
     s = w.spec
     out, lse = _run_oracle(w)
     bo, bl = brute.mla_decode_brute(w.q_bits, w.pool, w.block_table, w.seq_lens, kv_dtype=s.kv_dtype,
@@ -134,6 +135,12 @@ def pin_split_merge(seed=4):
 @pytest.mark.parametrize("s_q", [1, 2])
 def test_oracle_matches_brute_force(kv_dtype, s_q):
     pin_brute_force(kv_dtype, s_q)
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_oracle_matches_brute_force_on_the_528_byte_fp8_row(s_q):
+    # d_c = 448 + d_r = 64: the record's 512-dim row, 528 bytes, no padding
+    pin_brute_force("fp8", s_q, d_c=448)
 
 
 def test_absorbed_equals_unabsorbed():
