@@ -1,5 +1,6 @@
 """A seeded sweep of small random shapes through every decode path, against
-the float64 oracles: dense and sparse, bf16 and fp8 caches, page blocks
+the float64 oracles: dense and sparse, bf16, fp8 (also at the 448-d latent's
+528-byte row) and fp4 caches, page blocks
 16..256, 1..4 queries per sequence, 32..256 heads, forced worker counts,
 lengths on and off tile edges, and some flat-softmax queries (q = 0 or
 nearly), where a token wrongly masked in or out moves the output by about
@@ -18,12 +19,13 @@ from gpu_helpers import assert_parity, run_gpu, say
 pytestmark = pytest.mark.gpu
 
 N_CASES = 24
+N_CASES_D512 = 8     # the fp8 cache's 528-byte row (d_c = 448)
 
 
-def _case(seed: int):
-    rng = np.random.default_rng(1000 + seed)
-    kv = ("bf16", "fp8", "bf16", "fp4")[seed % 4]
-    sparse = seed % 8 >= 4
+def _case(seed: int, d512: bool = False):
+    rng = np.random.default_rng(1000 + seed + (500 if d512 else 0))
+    kv = "fp8" if d512 else ("bf16", "fp8", "bf16", "fp4")[seed % 4]
+    sparse = seed % 2 == 1 if d512 else seed % 8 >= 4
     page = int(rng.choice([16, 32, 64, 64, 128, 256]))
     s_q = int(rng.choice([1, 1, 2, 3, 4]))
     n_h = int(rng.choice([32, 64, 128, 128, 256]))
@@ -36,16 +38,18 @@ def _case(seed: int):
     q_scale = float(rng.choice([1.0, 1.0, 0.5, 0.02, 0.0]))
     topk = int(rng.choice([1, 40, 64, 100, 500, 2048])) if sparse else 0
     workers = int(rng.choice([0, 0, 1, 5, 37, 300]))
-    spec = WorkloadSpec(f"rand{seed}", batch, ("fixed", lens), kv_dtype=kv, s_q=s_q, n_h=n_h, page=page,
-                        q_scale=q_scale, spare_pages=3, topk=topk, seed=2000 + seed,
+    spec = WorkloadSpec(f"rand{seed}" + ("_d512" if d512 else ""), batch, ("fixed", lens), kv_dtype=kv, s_q=s_q,
+                        n_h=n_h, page=page, q_scale=q_scale, spare_pages=3, topk=topk,
+                        seed=2000 + seed + (500 if d512 else 0), d_c=448 if d512 else 512,
                         outlier_p=0.01 if kv != "bf16" else 0.0, outlier_mult=20.0)
     return spec, workers
 
 
-@pytest.mark.parametrize("seed", range(N_CASES))
-def test_random_shape(seed):
+@pytest.mark.parametrize("seed,d512", [(s, False) for s in range(N_CASES)] + [(s, True) for s in range(N_CASES_D512)],
+                         ids=[f"{s}" for s in range(N_CASES)] + [f"d512_{s}" for s in range(N_CASES_D512)])
+def test_random_shape(seed, d512):
     import torch
-    spec, workers = _case(seed)
+    spec, workers = _case(seed, d512)
     say(f"case {seed}: {spec} workers={workers}")
     w = make_workload(spec)
     s = w.spec
