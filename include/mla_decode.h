@@ -115,7 +115,8 @@ mla_status_t mla_decode_init(const mla_decode_params_t* params, mla_decode_handl
  * for `batch` sequences (0 <= batch <= max_batch).  `bytes` is a host pointer.
  * The workspace holds the per-call work plan and the split-KV partial results
  * (fp16 normalised outputs and fp32 LSEs of every context split); for the FP8
- * cache also the queries as two e4m3 terms (1216 bytes per query row). */
+ * cache also the queries as two e4m3 terms (two cache rows per query row:
+ * 1216 bytes at d_c = 512, 1056 at d_c = 448). */
 mla_status_t mla_decode_workspace_size(mla_decode_handle_t h, int32_t batch, size_t* bytes);
 
 /* mla_decode_run -- one decode step for `batch` sequences, all heads, all queries.
