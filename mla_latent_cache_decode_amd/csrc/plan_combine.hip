@@ -18,7 +18,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // One kernel shape, two instantiations chosen by the expected split count.
 // A block merges RPB rows; each row's splits are dealt to WPR waves in
-// contiguous ranges (WPR = 8, RPB = 1 for few long sequences with many
+// contiguous ranges (WPR = 4, RPB = 1 for few long sequences with many
 // splits; WPR = 1, RPB = 4 when sequences have few splits).  A lane owns 8
 // dims of the row: one 16-byte fp16 load per split (rows of d_c <= 512 dims;
 // lanes past d_c / 8 idle).
@@ -185,7 +185,10 @@ hipError_t launch_combine(const CombineArgs& a, int max_splits, hipStream_t stre
     // expected splits per sequence: the workers spread over the batch
     const int per_seq = max_splits / max(a.batch, 1);
     if (per_seq >= 32) {
-        hipLaunchKernelGGL((combine_kernel<8, 1, 16>), dim3((unsigned)(a.batch * a.rows)), dim3(512), 0, stream, a);
+        // four waves of 16 loads each cover 64 splits in one round (eight
+        // waves of 8: the same on the long-context step, 0.5 us slower on a
+        // single 1024-token sequence)
+        hipLaunchKernelGGL((combine_kernel<4, 1, 16>), dim3((unsigned)(a.batch * a.rows)), dim3(256), 0, stream, a);
     } else if (per_seq >= 6) {
         // lengths vary: the longest sequences have about twice the mean split count
         hipLaunchKernelGGL((combine_kernel<1, 4, 16>), dim3((unsigned)(a.batch * (a.rows / 4))), dim3(256), 0,
