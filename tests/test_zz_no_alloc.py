@@ -40,6 +40,10 @@ CASES = [
      WorkloadSpec("na_small_fp8", 2, ("fixed", (300, 65)), kv_dtype="fp8", spare_pages=2, seed=84)),
     (WorkloadSpec("na_big_mtp", 4, ("fixed", (5000, 2, 3000, 900)), s_q=2, spare_pages=4, seed=85),
      WorkloadSpec("na_small_mtp", 2, ("fixed", (100, 40)), s_q=2, spare_pages=2, seed=86)),
+    # the fp8 cache's 528-byte row (d_c = 448)
+    (WorkloadSpec("na_big_fp8_d512", 4, ("fixed", (5000, 1, 2600, 700)), kv_dtype="fp8", d_c=448, spare_pages=4,
+                  seed=87, outlier_p=0.01, outlier_mult=20.0),
+     WorkloadSpec("na_small_fp8_d512", 2, ("fixed", (200, 64)), kv_dtype="fp8", d_c=448, spare_pages=2, seed=88)),
 ]
 
 
