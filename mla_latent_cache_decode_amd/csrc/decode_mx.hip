@@ -21,11 +21,15 @@
 //    term in the cache's own row format.
 //  * Pages move HBM -> LDS raw (608-byte rows; 528 at the narrow latent
 //    width, see Fp8Dims) with direct-to-LDS buffer loads, double buffered:
-//    page p + 1 is fetched while tile p is computed.  In LDS a row is five
-//    128-byte column blocks (the last one also holds the first bytes of the
-//    next row, which are not used), token t's 16-byte chunk c at
-//    tile_off(t, c): conflict-free row reads.  Rows past the visible tokens
-//    are never fetched (the descriptor size excludes them).
+//    page p + 1 is fetched while tile p is computed.  With pages of 64
+//    tokens or more the tile is the page's bytes in order (each load one
+//    aligned KiB), up to a swap of chunk pairs that keeps row reads
+//    conflict-free (lin_flip).  Gathered rows (the sparse decode) and tiles
+//    made of several smaller pages use column blocks instead: a row is five
+//    128-byte blocks (the last one also holds the first bytes of the next
+//    row, which are not used), token t's 16-byte chunk c at tile_off(t, c).
+//    Rows past the visible tokens are never fetched (the descriptor size
+//    excludes them).
 //  * Q.K^T: wave w owns query rows 32w .. 32w + 31; per 64-deep k-step and
 //    32-token block one K fragment (32 bytes per lane from the raw page) and
 //    its scale bytes feed two scaled MFMAs (q_hi, q_lo).  The latent part of
@@ -72,6 +76,21 @@ struct MxShape {
     static_assert(kScaleChunk * 16 == F::kD && (kHiScales || F::kD / 32 <= 16), "scales follow the codes");
 };
 static_assert(MxShape<kDc>::kLds == 163840, "the kernel takes all of a CU's LDS at 512 dims");
+
+// Linear page layout (dense decode with pages of 64 tokens or more): the 64
+// rows of a tile lie in LDS as they lie in memory, so every 1 KiB load is one
+// aligned KiB of the page (eight whole 128-byte lines; loads of 128-byte row
+// pieces at a 608-byte stride straddle lines and cost the fp8_b64 decode
+// 189.5 -> 154.6 us, same box).  Rows of r chunks of 16 bytes: chunk c of
+// token t sits at chunk r t + (c ^ lin_flip(t, r)).  A 128-bit read of 16
+// consecutive tokens (t0 = 0 mod 16) at one chunk is served in one pass over
+// the 64 banks when the 16 chunk indices are distinct mod 16: with r = 33
+// (528-byte rows) r t = t mod 16 already is; with r = 38 (608-byte rows)
+// r t = 6 t mod 16 repeats after 8 tokens (even residues only), and the flip
+// moves tokens 8 .. 15 of each 16 to odd chunks.  The flip swaps the chunks
+// of a pair (2j, 2j + 1) of one row, which lie in one KiB of the page since
+// r t is even.  The flip is bit 3 of t for an even r, none for an odd r.
+__device__ __forceinline__ int lin_flip(int t, int r) { return (t >> 3) & ~r & 1; }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -235,6 +254,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
     constexpr int kMxScaleChunk = X::kScaleChunk;
     static_assert(kRowBytes <= kSparseZeroRowBytes, "the zero row covers a row");
     static_assert(Geom::kRangeTok % 16 == 0, "a wave's 16 tokens lie in one page");
+    // the tile is one run of 64 rows of one page: the linear layout
+    constexpr bool kLin = !kSparse && PS >= kPage;
+    constexpr int kR = X::kRowChunks;       // chunks of 16 bytes per row (38 / 33)
+    static_assert(kR * 16 == kRowBytes && kR * 1024 <= kMxRawBytes, "a linear page fits its buffer");
+    static_assert(kR <= 4 * kMxPiecesPerWave, "the waves' loads cover a page");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[X::kLds];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
     int* sbuf = (int*)smem;                 // planner scratch; dead before the first page lands
@@ -265,6 +289,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
     // of the piece's 8, the chunk whose swizzled slot is i & 7 (pieces of
     // odd token groups flip the slot's low bit: address ^ 16)
     const int dma_lane = (lane0 >> 3) * kRowBytes + (((lane0 & 7) ^ sw(lane0 >> 3)) << 4);
+    // linear layout: load k of wave w is the page's KiB 4k + w; its lane l
+    // writes chunk 64 (4k + w) + l = 256 k + lin_lane
+    const int lin_lane = 64 * wave + lane0;
 
     int64_t cost = start.cost;
     int slot_base = start.slot;
@@ -325,6 +352,22 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
                 lane_off = pinned(dma_lane) + flip;
             }
             dma16(r, lane_off + off, (uint32_t)(uintptr_t)(buf + cb * 8192 + g * 1024));
+        };
+        // linear layout: KiB i = 4k + w of the tile's rows (kR KiB in all);
+        // LDS chunk n holds the page's chunk n ^ lin_flip(n / kR) (the flip
+        // is an involution on a row's chunk pairs)
+        auto dma_lin = [&](__amdgpu_buffer_rsrc_t r, LDS_AS uint8_t* buf, auto k_c) {
+            constexpr int k = decltype(k_c)::value;
+            if constexpr (4 * k < kR) {
+                if (4 * k + 3 < kR || 4 * k + wave < kR) {
+                    const int n = 256 * k + pinned(lin_lane);
+                    dma16(r, (n ^ lin_flip(n / kR, kR)) << 4, (uint32_t)(uintptr_t)(buf + (4 * k + wave) * 1024));
+                }
+            }
+        };
+        auto dma_page = [&](__amdgpu_buffer_rsrc_t r, LDS_AS uint8_t* buf, auto k_c) {
+            if constexpr (kLin) dma_lin(r, buf, k_c);
+            else dma_piece(r, buf, k_c);
         };
 
         // sparse gather plan.  Unit b is query position j of sequence b_seq;
@@ -418,7 +461,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
             const int phys0 = load_phys(p_lo);
             phys_next = load_phys(p_lo + 1);
             const __amdgpu_buffer_rsrc_t r0 = page_rsrc(p_lo, phys0);
-            static_for<0, kMxPiecesPerWave>([&](auto k) { dma_piece(r0, raws[0], k); });
+            static_for<0, kMxPiecesPerWave>([&](auto k) { dma_page(r0, raws[0], k); });
         }
         // this wave's 32 query rows, both terms, as MFMA B operands: lane i
         // holds row i & 31, chunks 4s + h and 4s + 2 + h (h = i >> 5) of
@@ -479,18 +522,32 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
 
             const int lane = opaque_lane();
             const int h = lane >> 5;
+            // byte of (token t, chunk c) in the raw tile
+            auto raw_off = [&](int t, int c) {
+                if constexpr (kLin) return (kR * t + (c ^ lin_flip(t, kR))) << 4;
+                else return tile_off(t, c);
+            };
             // K fragment f = (k-step s = f >> 1, block f & 1): token 32 (f & 1) +
-            // (lane & 31), chunks 4s + h and 4s + 2 + h.  Chunk 4s + h + 2c sits
-            // in column block s / 2 at slot (4 (s & 1) + 2c + h) ^ sw(token):
-            // k_off[2 (s & 1) + c]; block 1's token is 32 further (same sw)
+            // (lane & 31), chunks 4s + h and 4s + 2 + h.  Column blocks: chunk
+            // 4s + h + 2c sits in column block s / 2 at slot (4 (s & 1) + 2c + h)
+            // ^ sw(token): k_off[2 (s & 1) + c]; block 1's token is 32 further
+            // (same sw).  Linear: the flip only touches the chunk's low bit (h),
+            // so k_off[0] + 64 s + 32 c (block 1: + 32 rows, same flip).
             int k_off[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) k_off[j] = tile_off(lane & 31, 2 * j + h);
+            for (int j = 0; j < 4; ++j) k_off[j] = raw_off(lane & 31, 2 * j + h);
             auto read_k = [&](auto f_c) -> i32x8 {
                 constexpr int f = decltype(f_c)::value, s = f >> 1, blk = f & 1;
-                const LDS_AS uint8_t* base = raw + (s >> 1) * 8192 + blk * 4096;
-                const u32x4 c0 = *(const LDS_AS u32x4*)(base + k_off[2 * (s & 1)]);
-                const u32x4 c1 = *(const LDS_AS u32x4*)(base + k_off[2 * (s & 1) + 1]);
+                u32x4 c0, c1;
+                if constexpr (kLin) {
+                    const LDS_AS uint8_t* base = raw + k_off[0] + blk * 32 * kRowBytes + 64 * s;
+                    c0 = *(const LDS_AS u32x4*)(base);
+                    c1 = *(const LDS_AS u32x4*)(base + 32);
+                } else {
+                    const LDS_AS uint8_t* base = raw + (s >> 1) * 8192 + blk * 4096;
+                    c0 = *(const LDS_AS u32x4*)(base + k_off[2 * (s & 1)]);
+                    c1 = *(const LDS_AS u32x4*)(base + k_off[2 * (s & 1) + 1]);
+                }
                 return i32x8{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2],
                              (int)c1[3]};
             };
@@ -499,22 +556,27 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
                 const int t = 32 * blk + (lane & 31);
-                const u32x4 slo = *(const LDS_AS u32x4*)(raw + tile_off(t, kMxScaleChunk));
-                const uint32_t shi = X::kHiScales ? *(const LDS_AS uint32_t*)(raw + tile_off(t, kMxScaleChunk + 1)) : 0u;
+                const u32x4 slo = *(const LDS_AS u32x4*)(raw + raw_off(t, kMxScaleChunk));
+                const uint32_t shi = X::kHiScales ? *(const LDS_AS uint32_t*)(raw + raw_off(t, kMxScaleChunk + 1)) : 0u;
                 ks[blk] = mx_scales(slo, shi, h);
             }
             // V dequantisation: lane i of wave w converts token 16w +
             // store_token(i & 15), chunks c = 4k + (i >> 4) (codes 16c .. 16c + 15, scale byte c / 2)
             // into fp16 chunks 2c, 2c + 1 of the V tile
             const int v_tok = 16 * wave + store_token(lane & 15);
-            const u32x4 v_sc = *(const LDS_AS u32x4*)(raw + tile_off(v_tok, kMxScaleChunk));
-            const int v_src = tile_off(v_tok, lane >> 4);           // chunk 4k + (i >> 4) adds k * 4 chunks
+            const u32x4 v_sc = *(const LDS_AS u32x4*)(raw + raw_off(v_tok, kMxScaleChunk));
+            const int v_src = raw_off(v_tok, lane >> 4);            // chunk 4k + (i >> 4) adds k * 4 chunks
             const int v_dst = tile_off(v_tok, 2 * (lane >> 4));
             u32x4 v_codes;
             auto v_read = [&](auto k_c) {
                 constexpr int k = decltype(k_c)::value;
-                // chunk 4k + j: column block k / 2, slot 4 (k & 1) + j (j = i >> 4)
-                v_codes = *(const LDS_AS u32x4*)(raw + (k >> 1) * 8192 + (v_src ^ ((4 * (k & 1)) << 4)));
+                if constexpr (kLin) {
+                    // 4k chunks further in the row; the flip keeps to bit 0
+                    v_codes = *(const LDS_AS u32x4*)(raw + v_src + 64 * k);
+                } else {
+                    // chunk 4k + j: column block k / 2, slot 4 (k & 1) + j (j = i >> 4)
+                    v_codes = *(const LDS_AS u32x4*)(raw + (k >> 1) * 8192 + (v_src ^ ((4 * (k & 1)) << 4)));
+                }
             };
             auto v_store = [&](auto k_c) {
                 constexpr int k = decltype(k_c)::value;
@@ -571,7 +633,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
                 if constexpr (f % 2 == 1 && f / 2 < kMxVPieces) v_store(std::integral_constant<int, f / 2>{});
                 if constexpr (f < kMxPiecesPerWave) {
                     if constexpr (kSparse) dma_sparse(rw_next, p + 1, rnext, std::integral_constant<int, f>{});
-                    else dma_piece(r_next, rnext, std::integral_constant<int, f>{});
+                    else dma_page(r_next, rnext, std::integral_constant<int, f>{});
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });

@@ -116,7 +116,8 @@ def _mx_lane_off(lane, gl, row_bytes):
 
 @pytest.mark.parametrize("row_bytes", [608, 528])
 def test_fp8_page_loads_write_their_own_chunks(row_bytes):
-    # piece k of wave w (page-block size >= 64): token group g = 2w + (k & 1),
+    # piece k of wave w (gathered rows; page-block size >= 64 shown): token
+    # group g = 2w + (k & 1),
     # column block k >> 1; LDS bytes cb * 8192 + g * 1024 + 16 i; five column
     # blocks of 8 chunks hold a row (608 or 528 bytes) and spare chunks
     for wave in range(4):
@@ -129,6 +130,101 @@ def test_fp8_page_loads_write_their_own_chunks(row_bytes):
                 byte = src - t * row_bytes
                 assert byte % 16 == 0 and 0 <= byte < 640, (wave, k, i, byte)
                 assert tile_off(t, byte // 16) == cb * 8192 + g * 1024 + 16 * i
+
+
+MX_SRC = os.path.join(ROOT, "mla_latent_cache_decode_amd", "csrc", "decode_mx.hip")
+
+
+def _lin_flip_body():
+    text = open(MX_SRC).read()
+    m = re.search(r"__device__ __forceinline__ int lin_flip\(int t, int r\) \{\s*return (.*?);\s*\}", text, flags=re.S)
+    assert m, f"lin_flip() not found in {MX_SRC}"
+    return m.group(1)
+
+
+_LIN_FLIP = _lin_flip_body()
+
+
+def lin_flip(t, r):
+    return eval(_LIN_FLIP, {}, {"t": t, "r": r})
+
+
+def lin_off(t, c, r):
+    # the block-scaled fp8 kernel's linear page layout (pages of 64 tokens
+    # and up): chunk c of token t at chunk r t + (c ^ lin_flip(t, r))
+    return (r * t + (c ^ lin_flip(t, r))) << 4
+
+
+@pytest.mark.parametrize("row_bytes", [608, 528])
+def test_linear_page_layout_is_a_bijection(row_bytes):
+    r = row_bytes // 16
+    offs = sorted(lin_off(t, c, r) for t in range(64) for c in range(r))
+    assert offs == list(range(0, 64 * row_bytes, 16))
+    # a row's chunks stay in the row, and pairs swap inside one KiB of the page
+    for t in range(64):
+        for c in range(r):
+            n = lin_off(t, c, r) // 16
+            assert n // r == t and n // 64 == (r * t + c) // 64
+
+
+@pytest.mark.parametrize("row_bytes", [608, 528])
+def test_linear_page_loads_each_read_one_aligned_kib_and_fill_the_tile(row_bytes):
+    # load k of wave w is KiB i = 4k + w of the tile's rows (loads past the
+    # page's r KiB are not issued); lane l writes LDS chunk 64 i + l and
+    # fetches the page's chunk n ^ lin_flip(n / r) -- the chunk the readers
+    # expect there
+    r = row_bytes // 16
+    where = {}
+    for wave in range(4):
+        for k in range(10):
+            i = 4 * k + wave
+            if i >= r:
+                continue
+            fetched = []
+            for lane in range(64):
+                n = 256 * k + 64 * wave + lane
+                m = n ^ lin_flip(n // r, r)
+                fetched.append(m)
+                where[m] = n
+            assert sorted(fetched) == list(range(64 * i, 64 * i + 64))
+    assert len(where) == 64 * r
+    for t in range(64):
+        for c in range(r):
+            assert where[r * t + c] * 16 == lin_off(t, c, r)
+
+
+@pytest.mark.parametrize("row_bytes", [608, 528])
+def test_linear_page_reads_are_conflict_free(row_bytes):
+    r = row_bytes // 16
+    dims = {608: 576, 528: 512}[row_bytes]         # codes per row; the latent part is dims - 64
+    # K fragments: lane l reads token 32 blk + (l & 31), chunks 4s + 2j + h
+    # (h = l >> 5), at k_off[0] + 64 s + 32 j + 32 rows per block
+    for blk in range(2):
+        for s in range(dims // 64):
+            for j in range(2):
+                addrs = []
+                for l in range(64):
+                    t, h = 32 * blk + (l & 31), l >> 5
+                    a = lin_off(l & 31, h, r) + blk * 32 * row_bytes + 64 * s + 32 * j
+                    assert a == lin_off(t, 4 * s + 2 * j + h, r)
+                    addrs.append(a)
+                assert _conflict_free(addrs, 16, 16), (blk, s, j)
+    # the scale chunk(s) of the same tokens
+    for blk in range(2):
+        for c in range(dims // 16, r):
+            assert _conflict_free([lin_off(32 * blk + (l & 31), c, r) for l in range(64)], 16, 16)
+    # V dequantisation: lane i of wave w reads token 16w + store_token(i & 15),
+    # chunks 4k + (i >> 4) at v_src + 64 k
+    store_token = lambda i: ((i & 7) << 1) | ((i >> 3) & 1)
+    for wave in range(4):
+        for k in range((dims - 64) // 64):
+            addrs = []
+            for i in range(64):
+                t = 16 * wave + store_token(i & 15)
+                a = lin_off(t, i >> 4, r) + 64 * k
+                assert a == lin_off(t, 4 * k + (i >> 4), r)
+                addrs.append(a)
+            assert _conflict_free(addrs, 16, 16), (wave, k)
 
 
 def test_dequantised_piece_stores_are_conflict_free():
