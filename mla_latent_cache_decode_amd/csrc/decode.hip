@@ -34,9 +34,9 @@
 //  * Both products run as fp16 MFMA with fp32 accumulation; queries are
 //    prescaled per head by a power of two into [2^14, 2^15) before the fp16
 //    conversion (exact) and the factor is folded into the softmax scale.
-//  * Lazy rescaling: the running max is only raised when a tile's max
-//    exceeds it by more than 15 (log2 units), so O is rarely rescaled after
-//    the first tile and the exponentials stay <= 2^15, inside fp16 range.
+//  * Lazy rescaling: the running max m is only raised when a tile's max
+//    exceeds it by more than 23 (log2 units), so O is rarely rescaled after
+//    the first tile; the weights 2^(s - m - 8) stay <= 2^15, inside fp16.
 #include "decode_rowsplit.h"
 
 namespace mla {

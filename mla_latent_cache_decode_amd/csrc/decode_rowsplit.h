@@ -13,7 +13,19 @@ namespace mla {
 namespace {
 
 constexpr int kPvSteps = 4 * kMdBlocks;         // 64 MFMA steps for P.V at 512 dims
-constexpr float kRescaleTau = 15.0f;            // log2 units: p <= 2^15 stays inside fp16
+// Lazy max with weights offset by 2^-8: the running max m of a row is raised
+// only when a tile's max exceeds it by more than kRescaleTau (log2 units), and
+// the fp16 weights are p = 2^(s - m - kPOffset) <= 2^(kRescaleTau - kPOffset)
+// = 2^15, inside fp16.  The offset cancels in O / l and is added back to the
+// LSE.  Without it the threshold could only be 15, and on the fp8 workload
+// with its 1 % of x20 outliers 11 % of a wave's tiles rescaled its 256 O
+// accumulators (each an AGPR read, multiply and write: fp8_b64 decode 185 ->
+// 153 us with the rescale skipped); a threshold of 23 cuts the tiles that
+// rescale about tenfold.  What the offset costs: weights below 2^-14 (s < m
+// - 6) are fp16 subnormals, rounded to 2^-25 absolute, i.e. 2^-17 of the
+// largest weight a tile at the running max holds.
+constexpr float kRescaleTau = 23.0f;
+constexpr float kPOffset = 8.0f;
 constexpr int kPvAhead = 2;                     // V fragment prefetch distance (steps)
 constexpr int kPMakeAt = 6;                     // P.V step (within a 16-step block) that builds the next P fragment
 
@@ -83,7 +95,7 @@ __device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveStat
     // P fragment kb (tokens of S^T registers 8(kb&1) .. +7 of s0 / s1) in
     // fp16; fragment 0 now, the others inside the P.V loop, where their
     // exponentials issue between MFMAs
-    const float neg_m = -st.m;
+    const float neg_m = -(st.m + kPOffset);
     float lsum = 0.f;
     auto make_p = [&](auto kb_c) -> f16x8 {
         constexpr int kb = decltype(kb_c)::value;
@@ -169,7 +181,7 @@ __device__ __forceinline__ void rowsplit_epilogue(const DecodeArgs& a, const Wav
     const int lane = opaque_lane();
     const float l_tot = pair_sum(st.l);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    const float lse_v = l_tot > 0.f ? (st.m + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
+    const float lse_v = l_tot > 0.f ? (st.m + kPOffset + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
                                     : -__builtin_inff();
     const int row = row0 + (lane & 31);
     const int hi = lane >> 5;
