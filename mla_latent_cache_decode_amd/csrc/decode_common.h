@@ -103,18 +103,46 @@ __device__ __forceinline__ void wg_barrier() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// x * alpha for an accumulator element that lives in an AGPR.  Written as
+// o * alpha for a 32x32 accumulator block that lives in AGPRs.  Written as
 // asm so the 256-register O accumulator keeps AGPRs as its home: a plain
 // VALU multiply would make the register allocator move all of O into arch
-// VGPRs and spill.  Only the (rare) lazy-rescale path uses it; the last MFMA
-// that wrote x is a whole tile (>= 72 MFMAs) earlier and the next MFMA that
-// reads it is behind the softmax, so no extra wait states are needed.
-__device__ __forceinline__ float scale_acc(float x, float alpha) {
-    float tmp;
-    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                 : "+a"(x), "=&v"(tmp)
-                 : "v"(alpha));
-    return x;
+// VGPRs and spill.  Only the lazy-rescale path uses it; the last MFMA that
+// wrote o is a whole tile (>= 72 MFMAs) earlier and the next MFMA that reads
+// it is behind the softmax, so no extra wait states are needed.
+// kGrouped: four elements per asm block (four reads, four multiplies, four
+// writes, each through its own temporary), so that the three steps of an
+// element do not wait on each other; one element per block serialises them
+// (about 5k cycles for the 256 elements of O), but leaves the register
+// allocator more freedom (the fp4 kernel spills inside its loop with the
+// grouped form).
+template <bool kGrouped>
+__device__ __forceinline__ void scale_acc16(f32x16& o, float alpha) {
+    if constexpr (!kGrouped) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float x = o[r], tmp;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(x), "=&v"(tmp)
+                         : "v"(alpha));
+            o[r] = x;
+        }
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float x0 = o[4 * q + 0], x1 = o[4 * q + 1], x2 = o[4 * q + 2], x3 = o[4 * q + 3];
+        float t0, t1, t2, t3;
+        asm volatile(
+            "v_accvgpr_read_b32 %4, %0\n\tv_accvgpr_read_b32 %5, %1\n\t"
+            "v_accvgpr_read_b32 %6, %2\n\tv_accvgpr_read_b32 %7, %3\n\t"
+            "v_mul_f32 %4, %4, %8\n\tv_mul_f32 %5, %5, %8\n\t"
+            "v_mul_f32 %6, %6, %8\n\tv_mul_f32 %7, %7, %8\n\t"
+            "v_accvgpr_write_b32 %0, %4\n\tv_accvgpr_write_b32 %1, %5\n\t"
+            "v_accvgpr_write_b32 %2, %6\n\tv_accvgpr_write_b32 %3, %7"
+            : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+            : "v"(alpha));
+        o[4 * q + 0] = x0; o[4 * q + 1] = x1; o[4 * q + 2] = x2; o[4 * q + 3] = x3;
+    }
 }
 
 // The lane id, hidden from loop-invariant code motion.  Lane-derived

@@ -642,7 +642,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
             __builtin_amdgcn_s_waitcnt(LGKMCNT0_IMM);
             wg_barrier();
 
-            softmax_pv<kSparse, F::kMdBlocks>(vt, st, s0, s1, n_valid, mk_cur, a.scale_log2, lane, [](auto) {});
+            softmax_pv<kSparse, F::kMdBlocks, true>(vt, st, s0, s1, n_valid, mk_cur, a.scale_log2, lane, [](auto) {});
             if constexpr (kSparse) {
                 mk_cur = mk_next;
                 mk_next = mk_after;

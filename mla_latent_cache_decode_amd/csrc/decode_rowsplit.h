@@ -19,11 +19,15 @@ constexpr int kPvSteps = 4 * kMdBlocks;         // 64 MFMA steps for P.V at 512 
 // = 2^15, inside fp16.  The offset cancels in O / l and is added back to the
 // LSE.  Without it the threshold could only be 15, and on the fp8 workload
 // with its 1 % of x20 outliers 11 % of a wave's tiles rescaled its 256 O
-// accumulators (each an AGPR read, multiply and write: fp8_b64 decode 185 ->
-// 153 us with the rescale skipped); a threshold of 23 cuts the tiles that
-// rescale about tenfold.  What the offset costs: weights below 2^-14 (s < m
-// - 6) are fp16 subnormals, rounded to 2^-25 absolute, i.e. 2^-17 of the
-// largest weight a tile at the running max holds.
+// accumulators (fp8_b64 decode 185 -> 153 us with the rescale skipped); a
+// threshold of 23 cuts the tiles that rescale about tenfold.  What the
+// offset costs: weights under 2^-14 (s < m - 6) are fp16 subnormals and
+// under 2^-25 (s < m - 17) zero.  On the fp8 workload's real scores, against
+// float64, twenty sequences give max |err| / RMS up to 1.1e-2, where no
+// offset gives up to 9.5e-3 (the fp8 bound is 4e-2).  The row sum l adds
+// the unrounded weights: summing the fp16-rounded ones instead is better
+// without an offset but, with it, lets a row whose weights are mostly
+// subnormal drift (up to 2.8e-2 on the same sequences).
 constexpr float kRescaleTau = 23.0f;
 constexpr float kPOffset = 8.0f;
 constexpr int kPvAhead = 2;                     // V fragment prefetch distance (steps)
@@ -46,13 +50,44 @@ struct WaveState {
 // the first n_valid (dense), or the set bits of `mask` (sparse: bit t =
 // token t).  Lazy rescaling: the running max is raised only when the tile's
 // max exceeds it by more than kRescaleTau, and O is then rescaled in place.
-// `lane` is the caller's opaque_lane().
-template <bool kSparse, int MD = kMdBlocks, typename PvHook>
+// `lane` is the caller's opaque_lane(); kGroupRescale picks scale_acc16's form.
+template <bool kSparse, int MD = kMdBlocks, bool kGroupRescale = false, typename PvHook>
 __device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveState<MD>& st, f32x16& s0, f32x16& s1,
                                            int n_valid, uint64_t mask, float scale_log2, int lane, PvHook&& pv_hook) {
     constexpr int kSteps = 4 * MD;              // P.V MFMA steps: 4 token blocks x MD dim blocks
     const int hi = lane >> 5;
     const LDS_AS uint8_t* tile = vtile;
+
+    // The first P.V steps' V^T fragments are read before the softmax, so
+    // that their LDS latency passes under it (the tile is complete: the
+    // callers' barrier).
+    // vp[m][e]: tokens 8e + tok (the swizzle sees bit 3 of the token, which
+    // flips the low slot bit: address ^ 16), dims m*32 + dim; the step's
+    // column block and 16-token block are added as immediate offsets
+    const LDS_AS uint8_t* vp[2][2];
+    {
+        const int g = lane >> 4, li = lane & 15;
+        const int tok = ((g >> 1) << 2) + (li >> 2);
+        const int dim = ((g & 1) << 4) + ((li & 3) << 2);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int o = tile_off(tok, (m * 32 + dim) >> 3) + (dim & 7) * 2;
+            vp[m][0] = tile + o;
+            vp[m][1] = tile + (o ^ 16) + 8 * 128;
+        }
+    }
+    constexpr int kVBufs = kPvAhead + 2;
+    f16x8 vf[kVBufs];
+    auto read_v = [&](auto step_c) -> f16x8 {
+        constexpr int step = decltype(step_c)::value;
+        constexpr int kb_ = step / MD, md = step % MD;
+        constexpr int off = (md >> 1) * 8192 + kb_ * 16 * 128;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][0] + off));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][1] + off));
+        return __builtin_bit_cast(f16x8, i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+    };
+    static_for<0, kPvAhead>([&](auto i) { vf[decltype(i)::value] = read_v(i); });
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- softmax.  Tokens >= n_valid (tail of the sequence / causal limit)
     // are masked: excluded from the max and given p = 0.  The token of
@@ -84,10 +119,7 @@ __device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveStat
         if (!st.o_zero) {
             const float alpha = need ? fast_exp2(st.m - m_new) : 1.0f;
 #pragma unroll
-            for (int md = 0; md < MD; ++md) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) st.o[md][r] = scale_acc(st.o[md][r], alpha);
-            }
+            for (int md = 0; md < MD; ++md) scale_acc16<kGroupRescale>(st.o[md], alpha);
             st.l *= alpha;
         }
         st.m = m_new;
@@ -118,32 +150,6 @@ __device__ __forceinline__ void softmax_pv(const LDS_AS uint8_t* vtile, WaveStat
     // fragment is two transposed reads (tokens kb*16 + e4*8 + tok_lane, dims
     // md*32 + dim_lane), issued kPvAhead steps ahead into rotating buffers.
     __builtin_amdgcn_sched_barrier(0);
-    // vp[m][e]: tokens 8e + tok (the swizzle sees bit 3 of the token, which
-    // flips the low slot bit: address ^ 16), dims m*32 + dim; the step's
-    // column block and 16-token block are added as immediate offsets
-    const LDS_AS uint8_t* vp[2][2];
-    {
-        const int g = lane >> 4, li = lane & 15;
-        const int tok = ((g >> 1) << 2) + (li >> 2);
-        const int dim = ((g & 1) << 4) + ((li & 3) << 2);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int o = tile_off(tok, (m * 32 + dim) >> 3) + (dim & 7) * 2;
-            vp[m][0] = tile + o;
-            vp[m][1] = tile + (o ^ 16) + 8 * 128;
-        }
-    }
-    constexpr int kVBufs = kPvAhead + 2;
-    f16x8 vf[kVBufs];
-    auto read_v = [&](auto step_c) -> f16x8 {
-        constexpr int step = decltype(step_c)::value;
-        constexpr int kb_ = step / MD, md = step % MD;
-        constexpr int off = (md >> 1) * 8192 + kb_ * 16 * 128;
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][0] + off));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[md & 1][1] + off));
-        return __builtin_bit_cast(f16x8, i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-    };
-    static_for<0, kPvAhead>([&](auto i) { vf[decltype(i)::value] = read_v(i); });
     static_for<0, kSteps>([&](auto step_c) {
         constexpr int step = decltype(step_c)::value;
         if constexpr (step + kPvAhead < kSteps)
