@@ -8,9 +8,10 @@ the decode's other roundings (fp16 weights) kept: one e4m3 term misses the
 4e-2 * RMS(out) bound by two orders of magnitude (the outliers multiply the
 query's rounding error, and sharp rows follow one token's score), while a
 two-term query q ~ q_hi + q_lo (each e4m3 with its own scales) is as
-accurate as the exact one -- but two scaled MFMAs per 64-deep k-block take
-the same matrix-core time as the fp16 MFMAs the fp8 kernel uses, so the
-block-scaled form buys nothing and the kernel keeps fp16 Q.K^T.
+accurate as the exact one.  The fp8 decode kernel therefore carries two
+query terms and issues two scaled MFMAs per 64-deep k-block: the same
+matrix-core time as fp16 MFMAs would take, but on the raw cache codes and
+scales, with no dequantisation of K.
 """
 
 import math
