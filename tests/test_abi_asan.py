@@ -21,7 +21,7 @@ def _env(lib, rt):
     env = dict(os.environ)
     env["MLA_DECODE_LIB_PATH"] = lib
     env["LD_PRELOAD"] = rt
-    # the interpreter's own allocations are not ours to judge
+    # the interpreter's own allocations are outside the library under test
     env["ASAN_OPTIONS"] = "detect_leaks=0:exitcode=86"
     return env
 
