@@ -18,6 +18,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["decode_bf16.hip", "decode.hip", "decode_mx.hip", "plan_combine.hip", "scratch.hip", "api.cpp"]
+# the matrix-core rate and clock probe: a library of its own, outside the decode path
+PROBE_SOURCE = "probe_mfma_clock.hip"
+PROBE_LIB_PATH = os.path.join(PKG, "libmla_probe.so")
 
 # per-source extra compiler flags
 SOURCE_FLAGS: dict = {}
@@ -60,6 +63,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmds.append([HIPCC] + flags + SOURCE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    probe_tmp = PROBE_LIB_PATH + ".tmp"
+    cmds.append([HIPCC] + flags + ["-shared", "-x", "hip", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_tmp])
     # the translation units compile independently: one hipcc each, in parallel
     jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
@@ -68,6 +73,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB_PATH)
+    os.replace(probe_tmp, PROBE_LIB_PATH)
     return LIB_PATH
 
 
