@@ -158,7 +158,11 @@ mla_status_t mla_decode_workspace_size(mla_decode_handle_t h, int32_t batch, siz
  * times its scale up to 61440); a larger one becomes infinite and the output
  * of its rows NaN.  Magnitudes below 2^-14 keep fewer significant bits, and
  * those below 2^-25 become zero; both are far below the output tolerance
- * whenever the values that dominate a row are of ordinary size.
+ * whenever the values that dominate a row are of ordinary size.  The
+ * softmax weights that P.V takes are fp16 as well, relative to a running
+ * maximum of the row's scores that is raised only when a score exceeds it
+ * by a large margin: a token whose weight is below 2^-17 (FP8 and FP4
+ * caches) or 2^-25 (BF16) of that maximum's contributes nothing.
  *
  * Split-KV: the context of a sequence is split across workers, and each
  * split's normalised partial output is stored as fp16 (relative rounding
