@@ -162,7 +162,7 @@ mla_status_t mla_decode_workspace_size(mla_decode_handle_t h, int32_t batch, siz
  * softmax weights that P.V takes are fp16 as well, relative to a running
  * maximum of the row's scores that is raised only when a score exceeds it
  * by a large margin: a token whose weight is below 2^-17 (FP8 and FP4
- * caches) or 2^-25 (BF16) of that maximum's contributes nothing.
+ * caches) or 2^-25 (BF16) of the weight at that maximum contributes nothing.
  *
  * Split-KV: the context of a sequence is split across workers, and each
  * split's normalised partial output is stored as fp16 (relative rounding
