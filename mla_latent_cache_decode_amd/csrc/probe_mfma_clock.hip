@@ -57,13 +57,9 @@ __global__ __launch_bounds__(256, 1) void probe_kernel(const float* __restrict__
     }
     const unsigned long long t1 = __builtin_amdgcn_s_memtime();
     const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
-    float s = 0.f;
+    // the accumulators are results as far as the compiler knows
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s += c[j][r];
-    // keep the accumulators live; a value no input produces never equals s
-    if (s == 1.2345e-37f) out[0] = 0;
+    for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(c[j]));
     if (lane == 0) {
         const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
         out[2 * w] = t1 - t0;
