@@ -79,17 +79,19 @@ static_assert(MxShape<kDc>::kLds == 163840, "the kernel takes all of a CU's LDS 
 
 // Linear page layout (dense decode with pages of 64 tokens or more): the 64
 // rows of a tile lie in LDS as they lie in memory, so every 1 KiB load is one
-// aligned KiB of the page (eight whole 128-byte lines; loads of 128-byte row
-// pieces at a 608-byte stride straddle lines and cost the fp8_b64 decode
-// 189.5 -> 154.6 us, same box).  Rows of r chunks of 16 bytes: chunk c of
-// token t sits at chunk r t + (c ^ lin_flip(t, r)).  A 128-bit read of 16
-// consecutive tokens (t0 = 0 mod 16) at one chunk is served in one pass over
-// the 64 banks when the 16 chunk indices are distinct mod 16: with r = 33
-// (528-byte rows) r t = t mod 16 already is; with r = 38 (608-byte rows)
-// r t = 6 t mod 16 repeats after 8 tokens (even residues only), and the flip
-// moves tokens 8 .. 15 of each 16 to odd chunks.  The flip swaps the chunks
-// of a pair (2j, 2j + 1) of one row, which lie in one KiB of the page since
-// r t is even.  The flip is bit 3 of t for an even r, none for an odd r.
+// aligned KiB of the page (eight whole 128-byte lines; 128-byte row pieces at
+// a 608- or 528-byte stride straddle lines: on fp8_b64 they fetched 392.6 MB
+// per decode against 359.1 MB now, and took 1.7x the L1 -> L2 requests; the
+// decode is 4 % faster at 528-byte rows, as fast at 608).  Rows of r chunks
+// of 16 bytes: chunk c of token t sits at chunk r t + (c ^ lin_flip(t, r)).
+// A 128-bit read of 16 consecutive tokens (t0 = 0 mod 16) at one chunk is
+// served in one pass over the 64 banks when the 16 chunk indices are
+// distinct mod 16: with r = 33 (528-byte rows) r t = t mod 16 already is;
+// with r = 38 (608-byte rows) r t = 6 t mod 16 repeats after 8 tokens (even
+// residues only), and the flip moves tokens 8 .. 15 of each 16 to odd
+// chunks.  The flip swaps the chunks of a pair (2j, 2j + 1) of one row,
+// which lie in one KiB of the page since r t is even.  The flip is bit 3 of
+// t for an even r, none for an odd r.
 __device__ __forceinline__ int lin_flip(int t, int r) { return (t >> 3) & ~r & 1; }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
