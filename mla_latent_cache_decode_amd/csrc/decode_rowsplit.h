@@ -22,9 +22,11 @@ constexpr int kPvSteps = 4 * kMdBlocks;         // 64 MFMA steps for P.V at 512 
 // accumulators (fp8_b64 decode 185 -> 153 us with the rescale skipped); a
 // threshold of 23 cuts the tiles that rescale about tenfold.  What the
 // offset costs: weights under 2^-14 (s < m - 6) are fp16 subnormals and
-// under 2^-25 (s < m - 17) zero.  On the fp8 workload's real scores, against
-// float64, twenty sequences give max |err| / RMS up to 1.1e-2, where no
-// offset gives up to 9.5e-3 (the fp8 bound is 4e-2).  The row sum l adds
+// under 2^-25 (s < m - 17) zero.  A CPU model of this arithmetic against
+// float64 (tests/test_softmax_weights_model.py, on the fp8 recipe's small
+// workload) gives max |err| / RMS 1.0e-2 with and without the offset, and on
+// twenty full-size fp8_b64 sequences up to 1.1e-2 with it and 9.5e-3
+// without (the fp8 bound is 4e-2).  The row sum l adds
 // the unrounded weights: summing the fp16-rounded ones instead is better
 // without an offset but, with it, lets a row whose weights are mostly
 // subnormal drift (up to 2.8e-2 on the same sequences).
