@@ -20,13 +20,16 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 24
 N_CASES_D512 = 8     # the fp8 cache's 528-byte row (d_c = 448)
+N_CASES_LIN = 8      # the fp8 dense decode with page blocks of 64 and up (its linear page layout), both row widths
 
 
-def _case(seed: int, d512: bool = False):
-    rng = np.random.default_rng(1000 + seed + (500 if d512 else 0))
-    kv = "fp8" if d512 else ("bf16", "fp8", "bf16", "fp4")[seed % 4]
-    sparse = seed % 2 == 1 if d512 else seed % 8 >= 4
-    page = int(rng.choice([16, 32, 64, 64, 128, 256]))
+def _case(seed: int, d512: bool = False, lin: bool = False):
+    if lin:
+        d512 = seed % 2 == 1
+    rng = np.random.default_rng(1000 + seed + (500 if d512 else 0) + (900 if lin else 0))
+    kv = "fp8" if d512 or lin else ("bf16", "fp8", "bf16", "fp4")[seed % 4]
+    sparse = False if lin else (seed % 2 == 1 if d512 else seed % 8 >= 4)
+    page = int(rng.choice([64, 128, 256] if lin else [16, 32, 64, 64, 128, 256]))
     s_q = int(rng.choice([1, 1, 2, 3, 4]))
     n_h = int(rng.choice([32, 64, 128, 128, 256]))
     batch = int(rng.integers(1, 6))
@@ -38,18 +41,21 @@ def _case(seed: int, d512: bool = False):
     q_scale = float(rng.choice([1.0, 1.0, 0.5, 0.02, 0.0]))
     topk = int(rng.choice([1, 40, 64, 100, 500, 2048])) if sparse else 0
     workers = int(rng.choice([0, 0, 1, 5, 37, 300]))
-    spec = WorkloadSpec(f"rand{seed}" + ("_d512" if d512 else ""), batch, ("fixed", lens), kv_dtype=kv, s_q=s_q,
-                        n_h=n_h, page=page, q_scale=q_scale, spare_pages=3, topk=topk,
-                        seed=2000 + seed + (500 if d512 else 0), d_c=448 if d512 else 512,
+    spec = WorkloadSpec(f"rand{seed}" + ("_lin" if lin else "") + ("_d512" if d512 else ""), batch, ("fixed", lens),
+                        kv_dtype=kv, s_q=s_q, n_h=n_h, page=page, q_scale=q_scale, spare_pages=3, topk=topk,
+                        seed=2000 + seed + (500 if d512 else 0) + (900 if lin else 0), d_c=448 if d512 else 512,
                         outlier_p=0.01 if kv != "bf16" else 0.0, outlier_mult=20.0)
     return spec, workers
 
 
-@pytest.mark.parametrize("seed,d512", [(s, False) for s in range(N_CASES)] + [(s, True) for s in range(N_CASES_D512)],
-                         ids=[f"{s}" for s in range(N_CASES)] + [f"d512_{s}" for s in range(N_CASES_D512)])
-def test_random_shape(seed, d512):
+@pytest.mark.parametrize("seed,d512,lin", [(s, False, False) for s in range(N_CASES)]
+                         + [(s, True, False) for s in range(N_CASES_D512)]
+                         + [(s, False, True) for s in range(N_CASES_LIN)],
+                         ids=[f"{s}" for s in range(N_CASES)] + [f"d512_{s}" for s in range(N_CASES_D512)]
+                         + [f"lin_{s}" for s in range(N_CASES_LIN)])
+def test_random_shape(seed, d512, lin):
     import torch
-    spec, workers = _case(seed, d512)
+    spec, workers = _case(seed, d512, lin)
     say(f"case {seed}: {spec} workers={workers}")
     w = make_workload(spec)
     s = w.spec
