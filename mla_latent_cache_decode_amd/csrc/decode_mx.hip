@@ -294,6 +294,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
     // linear layout: load k of wave w is the page's KiB 4k + w; its lane l
     // writes chunk 64 (4k + w) + l = 256 k + lin_lane
     const int lin_lane = 64 * wave + lane0;
+    const int lin16 = lin_lane << 4;
+    // bit 4 + k: the chunk flip of that lane in load k, formed once (each
+    // load then takes a shift, a bit select and an add instead of a
+    // division by the row's chunk count)
+    uint32_t lin_mask = 0;
+    if constexpr (kLin && kR % 2 == 0) {
+#pragma unroll
+        for (int k = 0; 4 * k < kR; ++k)
+            lin_mask |= (uint32_t)lin_flip((256 * k + lin_lane) / kR, kR) << (4 + k);
+    }
 
     int64_t cost = start.cost;
     int slot_base = start.slot;
@@ -362,8 +372,19 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void mla_decode_mx_kernel(Decode
             constexpr int k = decltype(k_c)::value;
             if constexpr (4 * k < kR) {
                 if (4 * k + 3 < kR || 4 * k + wave < kR) {
-                    const int n = 256 * k + pinned(lin_lane);
-                    dma16(r, (n ^ lin_flip(n / kR, kR)) << 4, (uint32_t)(uintptr_t)(buf + (4 * k + wave) * 1024));
+                    // (256 k + lin_lane) ^ flip, in bytes: the flip is bit 4
+                    // of the byte offset, which 4096 k leaves clear.  Three
+                    // instructions in one block (as separate expressions the
+                    // compiler hoists each load's flip out of the page loop
+                    // and spills it)
+                    int off;
+                    if constexpr (kR % 2 == 0)
+                        asm volatile("v_lshrrev_b32 %0, %1, %2\n\tv_and_b32 %0, 16, %0\n\tv_xad_u32 %0, %0, %3, %4"
+                                     : "=&v"(off)
+                                     : "n"(k), "v"(lin_mask), "v"(lin16), "s"(4096 * k));
+                    else
+                        off = pinned(lin16) + 4096 * k;
+                    dma16(r, off, (uint32_t)(uintptr_t)(buf + (4 * k + wave) * 1024));
                 }
             }
         };
