@@ -30,6 +30,8 @@ def _lib():
     lib.mla_probe_mfma_clock.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p]
     lib.mla_probe_mfma_clock.restype = ctypes.c_int
+    lib.mla_probe_mfma_valu.argtypes = lib.mla_probe_mfma_clock.argtypes
+    lib.mla_probe_mfma_valu.restype = ctypes.c_int
     return lib
 
 
@@ -38,6 +40,8 @@ def test_probe_rejects_bad_arguments_without_a_gpu_call():
     dummy = ctypes.c_void_p(16)
     for kind, grid, iters in ((2, 1, 1), (0, 0, 1), (0, 4097, 1), (1, 1, 0), (1, 1, 1000001)):
         assert lib.mla_probe_mfma_clock(kind, grid, iters, dummy, dummy, None) != 0
+    for kind, n, iters in ((2, 0, 1), (0, 3, 1), (1, 20, 1), (0, 4, 0), (1, 8, 1000001)):
+        assert lib.mla_probe_mfma_valu(kind, n, iters, dummy, dummy, None) != 0
 
 
 @pytest.mark.gpu
@@ -70,3 +74,32 @@ def test_mfma_issue_rate_is_fixed_and_the_clock_falls_with_load():
     print(f"{'instruction':36s} {'CUs':>4s} {'operands':>8s} {'cycles/MFMA/wave':>17s} {'clock GHz':>10s}")
     for n, g, d, c, f in rows:
         print(f"{n:36s} {g:4d} {d:>8s} {c:17.2f} {f:10.3f}")
+
+
+@pytest.mark.gpu
+def test_valu_instructions_under_a_running_mfma():
+    """One CU: a few conversions per MFMA issue free while the matrix core
+    works, more stretch the MFMA step (the hooks of the decode's tile loop
+    are priced by this)."""
+    import torch
+    lib = _lib()
+    dev = torch.device("cuda:0")
+    data = torch.tensor(np.random.default_rng(2).uniform(-1.0, 1.0, 1024), dtype=torch.float32, device=dev)
+    out = torch.zeros(4, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    cyc = {}
+    for kind in (0, 1):
+        for n in (0, 4, 8, 12, 16):
+            for _ in range(3):
+                assert lib.mla_probe_mfma_valu(kind, n, ITERS, data.data_ptr(), out.data_ptr(),
+                                               ctypes.c_void_p(stream.cuda_stream)) == 0
+            torch.cuda.synchronize()
+            cyc[kind, n] = float(np.median(out.cpu().numpy())) / (ITERS * 2)
+    print()
+    print(f"{'instruction':36s} " + " ".join(f"{n:>7d}" for n in (0, 4, 8, 12, 16)) + "  conversions per MFMA")
+    for kind in (0, 1):
+        print(f"{NAMES[1 - kind]:36s} " + " ".join(f"{cyc[kind, n]:7.2f}" for n in (0, 4, 8, 12, 16)))
+    assert abs(cyc[0, 0] / 64.0 - 1.0) <= 0.05 and abs(cyc[1, 0] / 32.0 - 1.0) <= 0.05
+    assert cyc[0, 4] <= 1.1 * cyc[0, 0]          # four hide under a 64-cycle MFMA
+    assert cyc[0, 16] >= 1.3 * cyc[0, 0]         # sixteen do not
+    assert cyc[1, 8] >= 1.3 * cyc[1, 0]          # eight do not under a 32-cycle one
